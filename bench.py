@@ -1,0 +1,189 @@
+"""Benchmark: one CSBP rank's BDLM-masked attention step (forward + backward)
+on one MI355X.
+
+A step is the whole per-rank path over one batch of synthetic input: the
+forward partial against every clean K/V shard, the LSE merge, the backward
+preparation, the backward against every shard and the dQ finalize.  Inputs
+are resident in HBM before the timed region.  Throughput counts useful
+(unmasked) pairs only: 4d flops per pair and q-head in the forward (QK^T, PV)
+and 10d in the backward (QK^T recompute, dO V^T, P^T dO, dS^T Q, dS K).
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+Prints one JSON line.  --gpus N with N > 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import contextlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BDLM attention fwd+bwd useful-pair TFLOP/s and % bf16 MFMA peak, 256K/rank"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+
+
+class EventTimer:
+    """HIP events on the current stream (the stream the library launches on) around each call."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.events = {}
+        self.enabled = False
+
+    @contextlib.contextmanager
+    def __call__(self, tag):
+        if not self.enabled:
+            yield
+            return
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        self.events.setdefault(tag, []).append((a, b))
+
+    def totals_ms(self):
+        self.torch.cuda.synchronize()
+        return {k: (sum(a.elapsed_time(b) for a, b in v), len(v)) for k, v in self.events.items()}
+
+
+def cpu_baseline_bdlm(cfg, inp_cpu, n_rows: int, seed: int = 0):
+    """The fp64 oracle on a sample of query rows (KV-head group 0, every key), timed on host cores."""
+    import numpy as np
+    import oracle
+    p = cfg.problem
+    G = p.h_q // p.h_kv
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(p.n_q, n_rows, replace=False))
+    f64 = lambda t: t.to(dtype=__import__("torch").float64).numpy()
+    q = f64(inp_cpu["q"][:, :G])
+    do = f64(inp_cpu["dout"][:, :G])
+    kc, vc = f64(inp_cpu["k_clean"][:, :1]), f64(inp_cpu["v_clean"][:, :1])
+    kx, vx = f64(inp_cpu["k_corr"][:, :1]), f64(inp_cpu["v_corr"][:, :1])
+    prob = dict(clean_len=p.clean_len, block_size=p.block_size, q_clean_offset=p.q_clean_offset,
+                q_clean_len=p.q_clean_len, owned_blocks=list(p.owned_blocks), kv_clean_offset=0,
+                kv_clean_len=p.clean_len, with_local_corrupt=True, scale=p.scale)
+    t0 = time.perf_counter()
+    o, lse = oracle.bdlm_fwd(prob, q, kc, vc, kx, vx, rows=rows)
+    D = oracle.delta_rows(o, do[rows])
+    oracle.bdlm_bwd(prob, q, kc, vc, kx, vx, do, lse, D, rows=rows)
+    dt = time.perf_counter() - t0
+    m = oracle.bdlm_mask(p.clean_len, p.block_size, p.q_clean_offset, p.q_clean_len, p.owned_blocks,
+                         0, p.clean_len, True, rows=rows)
+    pairs = int(m.sum()) * G
+    return dt, pairs, len(rows)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=32)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} refused: this BDLM attention path runs on one GPU "
+              "(one CSBP rank's share); multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from masked_long_context_amd import workloads as wl
+    from masked_long_context_amd.rank_step import BdlmRankStep
+
+    cfg = wl.config(args.config)
+    p = cfg.problem
+    print(f"# bench: generating inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = wl.bdlm_inputs(cfg, seed=0)
+    g = {k: v.cuda() for k, v in inp.items()}
+    step = BdlmRankStep(p, cfg.shards)
+    timer = EventTimer()
+    step.timer = timer
+    pairs = step.useful_pairs
+    flops = pairs * p.h_q * 14 * p.head_dim
+    args_ = (g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+    print(f"# bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step.step(*args_)
+    torch.cuda.synchronize()
+    timer.enabled = True
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step.step(*args_)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    tot = timer.totals_ms()
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    # dominant kernel: the backward (10d of the 14d flops per pair)
+    bwd_ms, bwd_n = tot.get("bwd", (0.0, 1))
+    bwd_flops_per_launch = pairs * p.h_q * 10 * p.head_dim / len(cfg.shards)
+    bwd_avg_ms = bwd_ms / bwd_n
+    bwd_achieved = bwd_flops_per_launch / (bwd_avg_ms * 1e-3) / 1e12
+    fwd_ms, fwd_n = tot.get("fwd", (0.0, 1))
+    fwd_achieved = pairs * p.h_q * 4 * p.head_dim * args.steps / (fwd_ms * 1e-3) / 1e12 if fwd_ms else 0.0
+    n_act = len(step.active)
+    merge_ms, merge_n = tot.get("merge", (0.0, 1))
+    merge_bytes = p.n_q * p.h_q * (n_act * (4 * p.head_dim + 4) + (2 * p.head_dim + 4))
+    merge_gbs = merge_bytes / (merge_ms / merge_n * 1e-3) / 1e9 if merge_ms else 0.0
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "clean_len": p.clean_len, "block_size": p.block_size,
+                   "q_rows": p.n_q, "h_q": p.h_q, "h_kv": p.h_kv, "head_dim": p.head_dim,
+                   "clean_shards": len(cfg.shards), "useful_pairs_per_head": pairs,
+                   "flops_per_step": flops},
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": "bwd_kernel<128>", "bound": "mfma", "achieved": round(bwd_achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "kernels": {
+            "bwd": {"ms_per_launch": round(bwd_avg_ms, 4), "launches_per_step": len(cfg.shards),
+                    "tflops": round(bwd_achieved, 2)},
+            "fwd": {"ms_per_step": round(fwd_ms / args.steps, 3), "launches_per_step": n_act,
+                    "tflops": round(fwd_achieved, 2)},
+            "merge": {"ms": round(merge_ms / max(merge_n, 1), 4), "parts": n_act, "gbs": round(merge_gbs, 1),
+                      "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4)},
+            "prepare_ms": round(tot.get("prepare", (0.0, 1))[0] / args.steps, 4),
+            "finalize_ms": round(tot.get("finalize", (0.0, 1))[0] / args.steps, 4),
+        },
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print(f"# bench: cpu baseline (oracle, {args.cpu_rows} sampled rows)", file=sys.stderr, flush=True)
+        dt, spairs, nrows = cpu_baseline_bdlm(cfg, inp, args.cpu_rows)
+        out["cpu_baseline"] = {"value": round(spairs * 14 * p.head_dim / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{nrows} seeded-random query rows x {p.h_q // p.h_kv} q-heads "
+                                         f"(KV group 0), all keys, fwd+bwd in fp64; {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

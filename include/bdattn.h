@@ -1,0 +1,192 @@
+/*
+ * bdattn.h -- C ABI of the MI355X (gfx950) BDLM-masked core attention library.
+ *
+ * What it computes.  softmax(Q K^T) V and its gradients for ONE rank's share of
+ * block-diffusion (BDLM) training under context-sharded block parallelism
+ * (CSBP), against one clean K/V range per call, plus the exact log-sum-exp
+ * merge of the per-range partials and a varlen entry point for packed shards.
+ *
+ *  - Mask: "rit.work explainer of CSBP", section on why conventional context
+ *    parallelism sends extra data: each corrupted (noised) target block sees
+ *    the clean prefix of the PRECEDING blocks and its own noised version;
+ *    corrupted K/V serve only the block that owns them.  "Block Parallelism
+ *    For Efficient Distributed Long-Context Diffusion Language Model
+ *    Training", English abstract: autoregressive across blocks, parallel
+ *    denoising within a block, so a clean token sees the clean tokens of its
+ *    own and all earlier blocks.  Exactly:
+ *        clean row at position p   -> clean key t iff t/B <= p/B
+ *        clean row                 -> corrupted key: never
+ *        corrupted block b (slot m)-> clean key t iff t/B <  b
+ *                                  -> corrupted key iff it is in slot m
+ *  - Sharding: the same abstract -- one rank owns each corrupted block, the
+ *    clean sequence is sharded by position across the ranks, corrupted K/V
+ *    stay local, and the training semantics are preserved; hence per-range
+ *    partials (O_s, LSE_s) merge exactly and the backward of a range uses the
+ *    merged LSE.
+ *  - Varlen: "Efficient Long-context Language Model Training by Core
+ *    Attention Disaggregation", English abstract: core attention over fused
+ *    batches of token-level shards of arbitrary length.
+ *
+ * Conventions.  scale <= 0 selects 1/sqrt(head_dim).  LSE is the natural-log
+ * sum of exp(scale * q.k) over the legal keys, fp32.  q-head h reads KV head
+ * h / (h_q / h_kv).  A row with no legal key gets O = 0 and LSE = -inf.
+ *
+ * Layouts (all row-major, contiguous in the last dimension):
+ *   Q, O, dO, dQ          [n_q][h_q][head_dim]  rows: the clean query rows,
+ *                                             then B rows per owned block in
+ *                                             owned_blocks order
+ *   K/V clean range       [kv_clean_len][h_kv][head_dim]  (pointer = first row of the range)
+ *   K/V local corrupted   [n_owned * B][h_kv][head_dim]   (same slot order as the rows)
+ *   LSE, delta            [h_q][n_q] fp32
+ *   packed varlen Q/O/dO  [total][h_q][head_dim], K/V [total][h_kv][head_dim]
+ * Tensors are bf16 unless stated.  Device pointers must be 16-byte aligned.
+ *
+ * Ownership.  Every device buffer, including the workspace and the prepare
+ * buffer, belongs to the caller; the library never allocates device memory.
+ * A plan holds host memory only (plus a pinned host copy of its tables, made
+ * on first use); it is immutable and may be shared between threads.  A plan
+ * must not be destroyed while work enqueued with it may still run
+ * (bdattn_plan_destroy waits for the device if the plan was ever used).
+ *
+ * Errors.  Every entry point returns a bdattn_status; no C++ exception crosses
+ * the ABI.  Arguments are validated before any HIP call (so validation runs on
+ * a machine without a GPU).  HIP failures map to BDATTN_EHIP.
+ * bdattn_last_error() returns a thread-local message for the last failure.
+ *
+ * Streams.  Every compute entry point is asynchronous on `stream` (0 = the
+ * null stream) and does not synchronize.
+ */
+#ifndef BDATTN_H
+#define BDATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BDATTN_OK = 0,
+  BDATTN_EINVAL = -1,        /* null pointer, negative size, bad head counts ...            */
+  BDATTN_EALIGN = -2,        /* offsets/lengths not multiples of block_size, misaligned ptr */
+  BDATTN_EUNSUPPORTED = -3,  /* head_dim not in {64, 128}, dtype not supported            */
+  BDATTN_EWORKSPACE = -4,    /* workspace / prepare buffer too small                       */
+  BDATTN_EHIP = -5           /* a HIP runtime call failed                                   */
+} bdattn_status;
+
+typedef enum { BDATTN_BF16 = 0, BDATTN_F32 = 1 } bdattn_dtype;
+
+/* One rank's BDLM problem against ONE clean K/V range. */
+typedef struct {
+  int64_t clean_len;          /* L: whole clean sequence length, multiple of block_size       */
+  int32_t block_size;         /* B >= 1                                                        */
+  int64_t q_clean_offset;     /* global position of the first clean query row, multiple of B  */
+  int64_t q_clean_len;        /* clean query rows (multiple of B, may be 0)                     */
+  const int64_t *owned_blocks;/* HOST array of n_owned global block ids in row order; each in
+                                 [0, L/B); copied by bdattn_plan_create                        */
+  int64_t n_owned;
+  int64_t kv_clean_offset;    /* first clean position of this call's K/V range (multiple of B)  */
+  int64_t kv_clean_len;       /* length of the range (multiple of B, may be 0)                  */
+  int32_t with_local_corrupt; /* 1: this call also attends the local corrupted K/V              */
+  int32_t h_q, h_kv;          /* h_q % h_kv == 0                                                */
+  int32_t head_dim;           /* 64 or 128                                                      */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim)                                  */
+} bdattn_problem;
+
+typedef struct bdattn_plan bdattn_plan;
+
+/* Build the host-side block-sparse tile schedule of a BDLM problem: the legal
+ * (query-tile, key-tile) pairs only, each marked full (no masked pair) or
+ * partial, longest tiles first.  *out receives a new plan. */
+int bdattn_plan_create(const bdattn_problem *problem, bdattn_plan **out);
+
+/* Plan for packed independent shards: cu_seqlens is a HOST int32 array of
+ * n_seqs + 1 non-decreasing offsets starting at 0; shard i owns rows and keys
+ * [cu[i], cu[i+1]).  causal = 1: row r sees keys cu[i] <= k <= r of its shard;
+ * causal = 0: all keys of its shard. */
+int bdattn_plan_create_varlen(const int32_t *cu_seqlens, int32_t n_seqs, int32_t causal,
+                              int32_t h_q, int32_t h_kv, int32_t head_dim, float softmax_scale,
+                              bdattn_plan **out);
+
+void bdattn_plan_destroy(bdattn_plan *plan);
+
+/* Sizes (bytes) of the per-call workspace and of the backward prepare buffer. */
+int64_t bdattn_plan_workspace_bytes(const bdattn_plan *plan);
+int64_t bdattn_plan_prepare_bytes(const bdattn_plan *plan);
+/* Legal (query, key) pairs per query head: the useful-work count. */
+int64_t bdattn_plan_useful_pairs(const bdattn_plan *plan);
+/* Query rows, and key rows of the clean (or packed) range and of the local corrupted K/V. */
+int64_t bdattn_plan_n_q(const bdattn_plan *plan);
+int64_t bdattn_plan_n_kv(const bdattn_plan *plan, int32_t segment /* 0 clean/packed, 1 corrupted */);
+
+/* Introspection of the schedule (for tests).  which:
+ *   0 row bounds : int32[n_q][4]  = {lo_a, hi_a, lo_b, hi_b}; row r may attend keys
+ *                  [lo_a, hi_a) of segment 0 and [lo_b, hi_b) of segment 1
+ *   1 fwd items  : int32[n][12]   = {q0, rows, seg0 lo_min, lo_max, hi_min, hi_max,
+ *                                    seg1 lo_min, lo_max, hi_min, hi_max, cost, 0}
+ *   2 bwd q-tiles: int32[n][12]   (same layout, backward query tiling)
+ *   3 bwd k-tiles: int32[n][4]    = {segment, k0, list_begin, list_end}
+ *   4 bwd list   : int32[n]       = q-tile index | (full << 31)
+ * Returns the number of records, or a negative status; copies at most `cap`
+ * records into `out` when out != NULL. */
+int64_t bdattn_plan_export(const bdattn_plan *plan, int32_t which, int32_t *out, int64_t cap);
+
+/* Forward partial of one clean K/V range (+ the local corrupted K/V when the
+ * plan's problem has with_local_corrupt).  Writes O ([n_q][h_q][d], o_dtype
+ * BDATTN_F32 or BDATTN_BF16) and LSE ([h_q][n_q] fp32) with `=`.
+ * k_corr/v_corr may be NULL when the plan has no local corrupted keys.
+ * workspace: >= bdattn_plan_workspace_bytes, 256-byte aligned. */
+int bdattn_fwd(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
+               const void *k_corr, const void *v_corr, void *o, int32_t o_dtype, float *lse,
+               void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Exact merge of n_parts partials over disjoint key sets:
+ *   m = max_s LSE_s;  LSE = m + ln sum_s exp(LSE_s - m);  O = sum_s exp(LSE_s - LSE) O_s
+ * (all partials -inf -> O = 0, LSE = -inf).  o_parts: [n_parts][n_rows][h][d] in
+ * part_dtype, lse_parts: [n_parts][h][n_rows] fp32; o_out [n_rows][h][d] in out_dtype,
+ * lse_out [h][n_rows] fp32.  d in {64, 128}. */
+int bdattn_lse_merge(int32_t n_parts, const void *o_parts, int32_t part_dtype, const float *lse_parts,
+                     int64_t n_rows, int32_t h, int32_t d, void *o_out, int32_t out_dtype,
+                     float *lse_out, void *stream);
+
+/* Backward preparation, once per rank step (shared by every K/V range):
+ * delta[h][r] = sum_d dO[r][h][d] * O[r][h][d] from the MERGED output O (o_dtype),
+ * and the transposed query-side tiles the backward reads, into `prepare`
+ * (>= bdattn_plan_prepare_bytes); when dq_accum is not NULL it is also cleared
+ * to 0 (fp32 [n_q][h_q][d]).  Any plan of the same query side (same clean query
+ * rows and owned blocks) may be used; the backward reads the tiles by index. */
+int bdattn_bwd_prepare(const bdattn_plan *plan, const void *q, const void *o, int32_t o_dtype,
+                       const void *dout, float *delta, float *dq_accum, void *prepare,
+                       int64_t prepare_bytes, void *stream);
+
+/* Backward of one K/V range given the MERGED lse and the prepared delta/tiles:
+ *   P = exp(S - LSE), dS = P o (dO V^T - delta)
+ *   dq_accum += scale dS K    (fp32 [n_q][h_q][d], accumulated with atomics across calls)
+ *   dk = scale dS^T Q, dv = P^T dO, summed over the q-heads of each KV head, written with `=`
+ *   (bf16) for every key of the range, zeros for keys no query attends.
+ * dk_corr/dv_corr may be NULL when the plan has no local corrupted keys. */
+int bdattn_bwd(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
+               const void *k_corr, const void *v_corr, const void *dout, const float *lse,
+               const float *delta, const void *prepare, int64_t prepare_bytes, float *dq_accum,
+               void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr, void *workspace,
+               int64_t workspace_bytes, void *stream);
+
+/* dq (bf16) = dq_accum (fp32), n_elems elements. */
+int bdattn_dq_finalize(const float *dq_accum, void *dq, int64_t n_elems, void *stream);
+
+/* Varlen packed shards: the same kernels over a plan from bdattn_plan_create_varlen. */
+int bdattn_varlen_fwd(const bdattn_plan *plan, const void *q, const void *k, const void *v, void *o,
+                      int32_t o_dtype, float *lse, void *workspace, int64_t workspace_bytes,
+                      void *stream);
+int bdattn_varlen_bwd(const bdattn_plan *plan, const void *q, const void *k, const void *v,
+                      const void *dout, const float *lse, const float *delta, const void *prepare,
+                      int64_t prepare_bytes, float *dq_accum, void *dk, void *dv, void *workspace,
+                      int64_t workspace_bytes, void *stream);
+
+/* Thread-local message describing the last non-OK status on this thread. */
+const char *bdattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BDATTN_H */

@@ -1,0 +1,394 @@
+// C ABI of the library: argument validation (before any HIP call), status
+// codes, thread-local error text, table uploads and kernel launches.
+#include "bdattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "kernels/kernels.h"
+#include "plan.h"
+
+struct bdattn_plan {
+  bdattn::Plan p;
+  std::mutex mu;   // guards the lazily made pinned copy of the tables
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+  g_err = msg;
+  return code;
+}
+
+int fail_build(const std::string &e) {
+  if (e.rfind("ALIGN:", 0) == 0) return fail(BDATTN_EALIGN, e.substr(6));
+  if (e.rfind("UNSUP:", 0) == 0) return fail(BDATTN_EUNSUPPORTED, e.substr(6));
+  return fail(BDATTN_EINVAL, e);
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(BDATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define CHECK(cond, code, msg) \
+  do {                         \
+    if (!(cond)) return fail(code, msg); \
+  } while (0)
+
+#define HIP_CHECK(expr, what)                    \
+  do {                                           \
+    hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+int check_ptr(const void *p, const char *name, bool needed) {
+  if (!needed) return BDATTN_OK;
+  if (!p) return fail(BDATTN_EINVAL, std::string(name) + " is NULL");
+  if (!aligned(p, 16)) return fail(BDATTN_EALIGN, std::string(name) + " is not 16-byte aligned");
+  return BDATTN_OK;
+}
+
+#define CHECK_PTR(p, needed)                          \
+  do {                                                \
+    int rc_ = check_ptr((p), #p, (needed));           \
+    if (rc_ != BDATTN_OK) return rc_;                 \
+  } while (0)
+
+int check_ws(const bdattn::Plan &p, const void *ws, int64_t bytes) {
+  if (!ws) return fail(BDATTN_EINVAL, "workspace is NULL");
+  if (!aligned(ws, BDATTN_ALIGN)) return fail(BDATTN_EALIGN, "workspace is not 256-byte aligned");
+  if (bytes < p.ws_bytes)
+    return fail(BDATTN_EWORKSPACE, "workspace too small: need " + std::to_string(p.ws_bytes) + " bytes");
+  return BDATTN_OK;
+}
+
+// Copies the plan's tables into the head of `dst` on `stream`.
+int upload(bdattn_plan *pl, void *dst, hipStream_t stream) {
+  bdattn::Plan &p = pl->p;
+  {
+    std::lock_guard<std::mutex> lk(pl->mu);
+    if (!p.pinned) {
+      void *h = nullptr;
+      HIP_CHECK(hipHostMalloc(&h, p.image.size(), hipHostMallocDefault), "hipHostMalloc");
+      std::memcpy(h, p.image.data(), p.image.size());
+      p.pinned = h;
+    }
+    p.used = true;
+  }
+  HIP_CHECK(hipMemcpyAsync(dst, p.pinned, p.image.size(), hipMemcpyHostToDevice, stream), "hipMemcpyAsync");
+  return BDATTN_OK;
+}
+
+const int32_t *img(const void *base, int64_t off) {
+  return reinterpret_cast<const int32_t *>((const char *)base + off);
+}
+
+int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
+            const void *v1, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
+  bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
+  const bdattn::Plan &p = pl->p;
+  CHECK(o_dtype == BDATTN_BF16 || o_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "o_dtype must be BF16 or F32");
+  const bool rows = p.n_q > 0;
+  CHECK_PTR(q, rows);
+  CHECK_PTR(o, rows);
+  CHECK_PTR(lse, rows);
+  CHECK_PTR(k0, p.n_seg[0] > 0);
+  CHECK_PTR(v0, p.n_seg[0] > 0);
+  CHECK_PTR(k1, p.n_seg[1] > 0);
+  CHECK_PTR(v1, p.n_seg[1] > 0);
+  int rc = check_ws(p, ws, ws_bytes);
+  if (rc != BDATTN_OK) return rc;
+  if (!rows) return BDATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  rc = upload(pl, ws, s);
+  if (rc != BDATTN_OK) return rc;
+  const void *kk[2] = {k0, k1}, *vv[2] = {v0, v1};
+  bdattn::FwdArgs a{};
+  for (int g = 0; g < 2; ++g) {
+    void *t = (char *)ws + p.ws_t_off[g];
+    if (p.n_seg[g] > 0) HIP_CHECK(bdattn::launch_transpose(vv[g], p.n_seg[g], p.h_kv, p.d, p.kpad[g], true, t, s), "transpose V");
+    a.k[g] = kk[g];
+    a.vt[g] = t;
+    a.kpad[g] = p.kpad[g];
+    a.n_seg[g] = (int32_t)p.n_seg[g];
+  }
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.rows = img(ws, p.hdr.off_rows);
+  a.items = img(ws, p.hdr.off_fwd);
+  a.n_items = p.hdr.n_fwd;
+  a.n_q = (int32_t)p.n_q;
+  a.h_q = p.h_q;
+  a.h_kv = p.h_kv;
+  a.group = p.h_q / p.h_kv;
+  a.o_f32 = o_dtype == BDATTN_F32;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  HIP_CHECK(bdattn::launch_fwd(a, p.d, s), "forward kernel");
+  return BDATTN_OK;
+}
+
+int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
+            const void *v1, const void *dout, const float *lse, const float *delta, const void *prep,
+            int64_t prep_bytes, float *dq, void *dk0, void *dv0, void *dk1, void *dv1, void *ws,
+            int64_t ws_bytes, void *stream) {
+  bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
+  const bdattn::Plan &p = pl->p;
+  const bool rows = p.n_q > 0;
+  const bool any_keys = p.n_seg[0] + p.n_seg[1] > 0;
+  const bool work = rows && any_keys;
+  CHECK_PTR(q, work);
+  CHECK_PTR(dout, work);
+  CHECK_PTR(lse, work);
+  CHECK_PTR(delta, work);
+  CHECK_PTR(dq, work);
+  CHECK_PTR(k0, p.n_seg[0] > 0);
+  CHECK_PTR(v0, p.n_seg[0] > 0);
+  CHECK_PTR(dk0, p.n_seg[0] > 0);
+  CHECK_PTR(dv0, p.n_seg[0] > 0);
+  CHECK_PTR(k1, p.n_seg[1] > 0);
+  CHECK_PTR(v1, p.n_seg[1] > 0);
+  CHECK_PTR(dk1, p.n_seg[1] > 0);
+  CHECK_PTR(dv1, p.n_seg[1] > 0);
+  if (work) {
+    CHECK(prep != nullptr, BDATTN_EINVAL, "prepare buffer is NULL");
+    CHECK(aligned(prep, BDATTN_ALIGN), BDATTN_EALIGN, "prepare buffer is not 256-byte aligned");
+    CHECK(prep_bytes >= p.prep_bytes, BDATTN_EWORKSPACE,
+          "prepare buffer too small: need " + std::to_string(p.prep_bytes) + " bytes");
+  }
+  int rc = check_ws(p, ws, ws_bytes);
+  if (rc != BDATTN_OK) return rc;
+  if (!any_keys) return BDATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  rc = upload(pl, ws, s);
+  if (rc != BDATTN_OK) return rc;
+  const void *kk[2] = {k0, k1}, *vv[2] = {v0, v1};
+  void *dk[2] = {dk0, dk1}, *dv[2] = {dv0, dv1};
+  bdattn::BwdArgs a{};
+  for (int g = 0; g < 2; ++g) {
+    void *t = (char *)ws + p.ws_t_off[g];
+    if (p.n_seg[g] > 0) HIP_CHECK(bdattn::launch_transpose(kk[g], p.n_seg[g], p.h_kv, p.d, p.kpad[g], false, t, s), "transpose K");
+    a.k[g] = kk[g];
+    a.v[g] = vv[g];
+    a.kt[g] = t;
+    a.kpad[g] = p.kpad[g];
+    a.n_seg[g] = (int32_t)p.n_seg[g];
+    a.dk[g] = dk[g];
+    a.dv[g] = dv[g];
+  }
+  a.q = q;
+  a.dout = dout;
+  a.qt = (const char *)prep + p.prep_q_off;
+  a.dot = (const char *)prep + p.prep_do_off;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.rows = img(ws, p.hdr.off_rows);
+  a.bq = img(ws, p.hdr.off_bq);
+  a.ktiles = img(ws, p.hdr.off_kt);
+  a.list = img(ws, p.hdr.off_list);
+  a.n_kt = p.hdr.n_kt;
+  a.n_bq = p.hdr.n_bq;
+  a.n_q = (int32_t)p.n_q;
+  a.h_q = p.h_q;
+  a.h_kv = p.h_kv;
+  a.group = p.h_q / p.h_kv;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  HIP_CHECK(bdattn::launch_bwd(a, p.d, s), "backward kernel");
+  return BDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bdattn_last_error(void) { return g_err.c_str(); }
+
+int bdattn_plan_create(const bdattn_problem *pr, bdattn_plan **out) {
+  if (!pr || !out) return fail(BDATTN_EINVAL, "problem or out is NULL");
+  try {
+    bdattn_plan *pl = new bdattn_plan;
+    std::string e = bdattn::build_bdlm(pl->p, pr->clean_len, pr->block_size, pr->q_clean_offset, pr->q_clean_len,
+                                       pr->owned_blocks, pr->n_owned, pr->kv_clean_offset, pr->kv_clean_len,
+                                       pr->with_local_corrupt != 0, pr->h_q, pr->h_kv, pr->head_dim,
+                                       pr->softmax_scale);
+    if (!e.empty()) {
+      delete pl;
+      return fail_build(e);
+    }
+    *out = pl;
+    return BDATTN_OK;
+  } catch (const std::bad_alloc &) {
+    return fail(BDATTN_EINVAL, "out of host memory building the plan");
+  } catch (const std::exception &x) {
+    return fail(BDATTN_EINVAL, x.what());
+  }
+}
+
+int bdattn_plan_create_varlen(const int32_t *cu, int32_t n_seqs, int32_t causal, int32_t h_q, int32_t h_kv,
+                              int32_t head_dim, float scale, bdattn_plan **out) {
+  if (!out) return fail(BDATTN_EINVAL, "out is NULL");
+  try {
+    bdattn_plan *pl = new bdattn_plan;
+    std::string e = bdattn::build_varlen(pl->p, cu, n_seqs, causal != 0, h_q, h_kv, head_dim, scale);
+    if (!e.empty()) {
+      delete pl;
+      return fail_build(e);
+    }
+    *out = pl;
+    return BDATTN_OK;
+  } catch (const std::bad_alloc &) {
+    return fail(BDATTN_EINVAL, "out of host memory building the plan");
+  } catch (const std::exception &x) {
+    return fail(BDATTN_EINVAL, x.what());
+  }
+}
+
+void bdattn_plan_destroy(bdattn_plan *pl) {
+  if (!pl) return;
+  if (pl->p.pinned) {
+    if (pl->p.used) (void)hipDeviceSynchronize();   // uploads may still read the pinned copy
+    (void)hipHostFree(pl->p.pinned);
+  }
+  delete pl;
+}
+
+int64_t bdattn_plan_workspace_bytes(const bdattn_plan *pl) { return pl ? pl->p.ws_bytes : BDATTN_EINVAL; }
+int64_t bdattn_plan_prepare_bytes(const bdattn_plan *pl) {
+  return pl ? pl->p.prep_bytes + (int64_t)pl->p.image.size() : BDATTN_EINVAL;
+}
+int64_t bdattn_plan_useful_pairs(const bdattn_plan *pl) { return pl ? pl->p.useful_pairs : BDATTN_EINVAL; }
+int64_t bdattn_plan_n_q(const bdattn_plan *pl) { return pl ? pl->p.n_q : BDATTN_EINVAL; }
+int64_t bdattn_plan_n_kv(const bdattn_plan *pl, int32_t seg) {
+  if (!pl || seg < 0 || seg > 1) return fail(BDATTN_EINVAL, "bad plan or segment");
+  return pl->p.n_seg[seg];
+}
+
+int64_t bdattn_plan_export(const bdattn_plan *pl, int32_t which, int32_t *out, int64_t cap) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  const bdattn::Plan &p = pl->p;
+  const int32_t *src = nullptr;
+  int64_t n = 0, w = 0;
+  switch (which) {
+    case 0: src = p.rows.data(); n = p.n_q; w = 4; break;
+    case 1: src = reinterpret_cast<const int32_t *>(p.fwd.data()); n = (int64_t)p.fwd.size(); w = 12; break;
+    case 2: src = reinterpret_cast<const int32_t *>(p.bq.data()); n = (int64_t)p.bq.size(); w = 12; break;
+    case 3: src = reinterpret_cast<const int32_t *>(p.kt.data()); n = (int64_t)p.kt.size(); w = 4; break;
+    case 4: src = p.list.data(); n = (int64_t)p.list.size(); w = 1; break;
+    default: return fail(BDATTN_EINVAL, "which must be 0..4");
+  }
+  if (out && n > 0) std::memcpy(out, src, (size_t)(std::min(n, cap) * w * 4));
+  return n;
+}
+
+int bdattn_fwd(const bdattn_plan *pl, const void *q, const void *k_clean, const void *v_clean, const void *k_corr,
+               const void *v_corr, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  if (pl->p.kind != 0) return fail(BDATTN_EINVAL, "plan is a varlen plan; use bdattn_varlen_fwd");
+  return run_fwd(pl, q, k_clean, v_clean, k_corr, v_corr, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int bdattn_varlen_fwd(const bdattn_plan *pl, const void *q, const void *k, const void *v, void *o, int32_t o_dtype,
+                      float *lse, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  if (pl->p.kind != 1) return fail(BDATTN_EINVAL, "plan is not a varlen plan; use bdattn_fwd");
+  return run_fwd(pl, q, k, v, nullptr, nullptr, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int bdattn_bwd(const bdattn_plan *pl, const void *q, const void *k_clean, const void *v_clean, const void *k_corr,
+               const void *v_corr, const void *dout, const float *lse, const float *delta, const void *prep,
+               int64_t prep_bytes, float *dq, void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr,
+               void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  if (pl->p.kind != 0) return fail(BDATTN_EINVAL, "plan is a varlen plan; use bdattn_varlen_bwd");
+  return run_bwd(pl, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, prep, prep_bytes, dq, dk_clean,
+                 dv_clean, dk_corr, dv_corr, ws, ws_bytes, stream);
+}
+
+int bdattn_varlen_bwd(const bdattn_plan *pl, const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, const float *delta, const void *prep, int64_t prep_bytes, float *dq,
+                      void *dk, void *dv, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  if (pl->p.kind != 1) return fail(BDATTN_EINVAL, "plan is not a varlen plan; use bdattn_bwd");
+  return run_bwd(pl, q, k, v, nullptr, nullptr, dout, lse, delta, prep, prep_bytes, dq, dk, dv, nullptr, nullptr,
+                 ws, ws_bytes, stream);
+}
+
+int bdattn_bwd_prepare(const bdattn_plan *cpl, const void *q, const void *o, int32_t o_dtype, const void *dout,
+                       float *delta, float *dq_accum, void *prep, int64_t prep_bytes, void *stream) {
+  if (!cpl) return fail(BDATTN_EINVAL, "plan is NULL");
+  bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
+  const bdattn::Plan &p = pl->p;
+  CHECK(o_dtype == BDATTN_BF16 || o_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "o_dtype must be BF16 or F32");
+  const bool rows = p.n_q > 0;
+  CHECK_PTR(q, rows);
+  CHECK_PTR(o, rows);
+  CHECK_PTR(dout, rows);
+  CHECK_PTR(delta, rows);
+  if (dq_accum) CHECK_PTR(dq_accum, rows);
+  CHECK(prep != nullptr, BDATTN_EINVAL, "prepare buffer is NULL");
+  CHECK(aligned(prep, BDATTN_ALIGN), BDATTN_EALIGN, "prepare buffer is not 256-byte aligned");
+  const int64_t need = p.prep_bytes + (int64_t)p.image.size();
+  CHECK(prep_bytes >= need, BDATTN_EWORKSPACE, "prepare buffer too small: need " + std::to_string(need) + " bytes");
+  if (!rows) return BDATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char *table = (char *)prep + p.prep_bytes;    // tables after the slabs
+  int rc = upload(pl, table, s);
+  if (rc != BDATTN_OK) return rc;
+  bdattn::PrepArgs a{};
+  a.q = q;
+  a.o = o;
+  a.dout = dout;
+  a.o_f32 = o_dtype == BDATTN_F32;
+  a.delta = delta;
+  a.dq_zero = dq_accum;
+  a.qt = (char *)prep + p.prep_q_off;
+  a.dot = (char *)prep + p.prep_do_off;
+  a.bq = img(table, p.hdr.off_bq);
+  a.n_bq = p.hdr.n_bq;
+  a.n_q = (int32_t)p.n_q;
+  a.h_q = p.h_q;
+  HIP_CHECK(bdattn::launch_prepare(a, p.d, s), "prepare kernel");
+  return BDATTN_OK;
+}
+
+int bdattn_dq_finalize(const float *acc, void *dq, int64_t n, void *stream) {
+  CHECK(n >= 0, BDATTN_EINVAL, "n_elems must be >= 0");
+  CHECK_PTR(acc, n > 0);
+  CHECK_PTR(dq, n > 0);
+  if (n == 0) return BDATTN_OK;
+  HIP_CHECK(bdattn::launch_dq_finalize(acc, dq, n, (hipStream_t)stream), "dq finalize kernel");
+  return BDATTN_OK;
+}
+
+int bdattn_lse_merge(int32_t n_parts, const void *o_parts, int32_t part_dtype, const float *lse_parts,
+                     int64_t n_rows, int32_t h, int32_t d, void *o_out, int32_t out_dtype, float *lse_out,
+                     void *stream) {
+  CHECK(n_parts >= 1, BDATTN_EINVAL, "n_parts must be >= 1");
+  CHECK(n_rows >= 0 && h >= 1, BDATTN_EINVAL, "n_rows must be >= 0 and h >= 1");
+  CHECK(d == 64 || d == 128, BDATTN_EUNSUPPORTED, "d must be 64 or 128");
+  CHECK(part_dtype == BDATTN_BF16 || part_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "part_dtype must be BF16 or F32");
+  CHECK(out_dtype == BDATTN_BF16 || out_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "out_dtype must be BF16 or F32");
+  const bool any = n_rows > 0;
+  CHECK_PTR(o_parts, any);
+  CHECK_PTR(lse_parts, any);
+  CHECK_PTR(o_out, any);
+  CHECK_PTR(lse_out, any);
+  if (!any) return BDATTN_OK;
+  HIP_CHECK(bdattn::launch_merge(n_parts, o_parts, part_dtype == BDATTN_F32, lse_parts, n_rows, h, d, o_out,
+                                 out_dtype == BDATTN_F32, lse_out, (hipStream_t)stream),
+            "merge kernel");
+  return BDATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Host-side block-sparse tile scheduler.
+//
+// The BDLM mask gives every query row a contiguous legal key range in each key
+// segment (a clean K/V range, and the local corrupted K/V), see the mask rules
+// in bdattn.h ("rit.work explainer of CSBP", section on why conventional
+// context parallelism sends extra data; "Block Parallelism For Efficient
+// Distributed Long-Context Diffusion Language Model Training", English
+// abstract).  The scheduler stores those ranges per row, tiles the rows, and
+// keeps only the (query-tile, key-tile) pairs that hold a legal pair.  Each
+// kept pair is marked full (no masked pair inside) or partial.  Tiles are
+// ordered longest first so that the dispatcher's in-order launch approximates
+// longest-processing-time balancing; with the early+late block pairing of the
+// same explainer this keeps the per-tile cost spread small.
+#include "plan.h"
+
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+
+namespace bdattn {
+
+namespace {
+
+std::atomic<uint64_t> g_next_id{1};
+
+struct Region { int64_t begin, end; };   // query rows tiled together
+
+void summarize(const std::vector<int32_t> &rows, int64_t q0, int64_t n, TileDesc &t) {
+  t.q0 = (int32_t)q0;
+  t.rows = (int32_t)n;
+  for (int s = 0; s < 2; ++s) {
+    int32_t lo_min = INT32_MAX, hi_max = INT32_MIN, lo_max = INT32_MIN, hi_min = INT32_MAX;
+    bool any = false;
+    for (int64_t r = q0; r < q0 + n; ++r) {
+      int32_t lo = rows[r * 4 + 2 * s], hi = rows[r * 4 + 2 * s + 1];
+      if (hi > lo) {
+        any = true;
+        lo_min = std::min(lo_min, lo);
+        hi_max = std::max(hi_max, hi);
+        lo_max = std::max(lo_max, lo);
+        hi_min = std::min(hi_min, hi);
+      } else {
+        hi_min = 0;                 // an empty row: no key tile is full
+        lo_max = std::max(lo_max, 0);
+      }
+    }
+    if (!any) t.seg[s] = SegSummary{0, 0, 0, 0};
+    else t.seg[s] = SegSummary{lo_min, lo_max, hi_min, hi_max};
+  }
+}
+
+int32_t tiles_in(const SegSummary &s, int bn) {
+  if (s.hi_max <= s.lo_min) return 0;
+  int64_t a = s.lo_min / bn, b = (s.hi_max + bn - 1) / bn;
+  return (int32_t)(b - a);
+}
+
+void tile_regions(Plan &p, const std::vector<Region> &regions) {
+  p.fwd.clear();
+  p.bq.clear();
+  for (const Region &g : regions) {
+    for (int64_t q0 = g.begin; q0 < g.end; q0 += BDATTN_FWD_BM) {
+      TileDesc t{};
+      summarize(p.rows, q0, std::min<int64_t>(BDATTN_FWD_BM, g.end - q0), t);
+      t.cost = tiles_in(t.seg[0], BDATTN_FWD_BN) + tiles_in(t.seg[1], BDATTN_FWD_BN);
+      p.fwd.push_back(t);
+    }
+    for (int64_t q0 = g.begin; q0 < g.end; q0 += BDATTN_BWD_BM) {
+      TileDesc t{};
+      summarize(p.rows, q0, std::min<int64_t>(BDATTN_BWD_BM, g.end - q0), t);
+      t.cost = 0;
+      p.bq.push_back(t);
+    }
+  }
+  std::stable_sort(p.fwd.begin(), p.fwd.end(),
+                   [](const TileDesc &a, const TileDesc &b) { return a.cost > b.cost; });
+}
+
+void build_bwd_lists(Plan &p) {
+  const int bn = BDATTN_BWD_BN;
+  int64_t nkt[2] = {(p.n_seg[0] + bn - 1) / bn, (p.n_seg[1] + bn - 1) / bn};
+  int64_t n_tiles = nkt[0] + nkt[1];
+  std::vector<int64_t> count(n_tiles + 1, 0);
+  auto tile_index = [&](int s, int64_t k) { return (s == 0 ? 0 : nkt[0]) + k; };
+  for (const TileDesc &t : p.bq)
+    for (int s = 0; s < 2; ++s) {
+      const SegSummary &g = t.seg[s];
+      if (g.hi_max <= g.lo_min) continue;
+      for (int64_t k = g.lo_min / bn; k * bn < g.hi_max; ++k) count[tile_index(s, k) + 1]++;
+    }
+  for (int64_t i = 0; i < n_tiles; ++i) count[i + 1] += count[i];
+  p.list.assign(count[n_tiles], 0);
+  std::vector<int64_t> fill(count.begin(), count.end() - 1);
+  for (size_t qi = 0; qi < p.bq.size(); ++qi) {
+    const TileDesc &t = p.bq[qi];
+    for (int s = 0; s < 2; ++s) {
+      const SegSummary &g = t.seg[s];
+      if (g.hi_max <= g.lo_min) continue;
+      for (int64_t k = g.lo_min / bn; k * bn < g.hi_max; ++k) {
+        int64_t k0 = k * bn, k1 = k0 + bn;
+        bool full = g.lo_max <= k0 && k1 <= g.hi_min;
+        p.list[fill[tile_index(s, k)]++] = (int32_t)qi | (full ? INT32_MIN : 0);
+      }
+    }
+  }
+  p.kt.clear();
+  for (int s = 0; s < 2; ++s)
+    for (int64_t k = 0; k < nkt[s]; ++k) {
+      int64_t i = tile_index(s, k);
+      p.kt.push_back(KTile{s, (int32_t)(k * bn), (int32_t)count[i], (int32_t)count[i + 1]});
+    }
+  std::stable_sort(p.kt.begin(), p.kt.end(), [](const KTile &a, const KTile &b) {
+    return (a.end - a.begin) > (b.end - b.begin);
+  });
+}
+
+void finish(Plan &p) {
+  p.useful_pairs = 0;
+  for (int64_t r = 0; r < p.n_q; ++r)
+    for (int s = 0; s < 2; ++s)
+      p.useful_pairs += std::max<int64_t>(0, (int64_t)p.rows[r * 4 + 2 * s + 1] - p.rows[r * 4 + 2 * s]);
+  build_bwd_lists(p);
+
+  // Device image: header | rows | fwd items | bwd q-tiles | bwd k-tiles | bwd list.
+  ImageHeader &h = p.hdr;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = BDATTN_IMAGE_MAGIC;
+  h.n_q = (int32_t)p.n_q;
+  h.n_fwd = (int32_t)p.fwd.size();
+  h.n_bq = (int32_t)p.bq.size();
+  h.n_kt = (int32_t)p.kt.size();
+  h.n_list = (int32_t)p.list.size();
+  h.n_seg0 = (int32_t)p.n_seg[0];
+  h.n_seg1 = (int32_t)p.n_seg[1];
+  int64_t off = align_up(sizeof(ImageHeader), BDATTN_ALIGN);
+  h.off_rows = off;  off = align_up(off + (int64_t)p.rows.size() * 4, BDATTN_ALIGN);
+  h.off_fwd = off;   off = align_up(off + (int64_t)p.fwd.size() * sizeof(TileDesc), BDATTN_ALIGN);
+  h.off_bq = off;    off = align_up(off + (int64_t)p.bq.size() * sizeof(TileDesc), BDATTN_ALIGN);
+  h.off_kt = off;    off = align_up(off + (int64_t)p.kt.size() * sizeof(KTile), BDATTN_ALIGN);
+  h.off_list = off;  off = align_up(off + (int64_t)p.list.size() * 4, BDATTN_ALIGN);
+  h.image_bytes = off;
+  p.image.assign(off, 0);
+  std::memcpy(p.image.data(), &h, sizeof(h));
+  if (!p.rows.empty()) std::memcpy(p.image.data() + h.off_rows, p.rows.data(), p.rows.size() * 4);
+  if (!p.fwd.empty()) std::memcpy(p.image.data() + h.off_fwd, p.fwd.data(), p.fwd.size() * sizeof(TileDesc));
+  if (!p.bq.empty()) std::memcpy(p.image.data() + h.off_bq, p.bq.data(), p.bq.size() * sizeof(TileDesc));
+  if (!p.kt.empty()) std::memcpy(p.image.data() + h.off_kt, p.kt.data(), p.kt.size() * sizeof(KTile));
+  if (!p.list.empty()) std::memcpy(p.image.data() + h.off_list, p.list.data(), p.list.size() * 4);
+
+  // Workspace: image | transposed K or V of segment 0 | of segment 1.
+  off = h.image_bytes;
+  for (int s = 0; s < 2; ++s) {
+    p.kpad[s] = align_up(p.n_seg[s], BDATTN_KPAD);
+    p.ws_t_off[s] = off;
+    off = align_up(off + (int64_t)p.h_kv * p.d * p.kpad[s] * 2, BDATTN_ALIGN);
+  }
+  p.ws_bytes = off;
+  // Prepare buffer: per backward q-tile, transposed Q and dO slabs [h_q][d][BM].
+  int64_t slab = (int64_t)p.bq.size() * p.h_q * p.d * BDATTN_BWD_BM * 2;
+  p.prep_q_off = 0;
+  p.prep_do_off = align_up(slab, BDATTN_ALIGN);
+  p.prep_bytes = p.prep_do_off + align_up(slab, BDATTN_ALIGN);
+  p.id = g_next_id.fetch_add(1);
+}
+
+std::string check_heads(int32_t h_q, int32_t h_kv, int32_t d) {
+  if (h_q <= 0 || h_kv <= 0) return "h_q and h_kv must be positive";
+  if (h_q % h_kv) return "h_q must be a multiple of h_kv";
+  if (d != 64 && d != 128) return "UNSUP:head_dim must be 64 or 128";
+  return "";
+}
+
+}  // namespace
+
+std::string build_bdlm(Plan &p, int64_t L, int32_t B, int64_t q_off, int64_t q_len,
+                       const int64_t *owned, int64_t n_owned, int64_t kv_off, int64_t kv_len,
+                       bool local, int32_t h_q, int32_t h_kv, int32_t d, float scale) {
+  if (L <= 0 || B <= 0) return "clean_len and block_size must be positive";
+  if (L % B) return "ALIGN:clean_len must be a multiple of block_size";
+  if (q_off < 0 || q_len < 0 || q_off + q_len > L) return "clean query range outside [0, clean_len]";
+  if (q_off % B || q_len % B) return "ALIGN:clean query range must be made of whole blocks";
+  if (kv_off < 0 || kv_len < 0 || kv_off + kv_len > L) return "clean K/V range outside [0, clean_len]";
+  if (kv_off % B || kv_len % B) return "ALIGN:clean K/V range must be made of whole blocks";
+  if (n_owned < 0 || (n_owned > 0 && !owned)) return "owned_blocks is NULL";
+  const int64_t nb = L / B;
+  for (int64_t m = 0; m < n_owned; ++m)
+    if (owned[m] < 0 || owned[m] >= nb) return "owned block id outside [0, clean_len / block_size)";
+  std::string e = check_heads(h_q, h_kv, d);
+  if (!e.empty()) return e;
+  const int64_t n_q = q_len + n_owned * (int64_t)B;
+  const int64_t n_corr = local ? n_owned * (int64_t)B : 0;
+  if (n_q > INT32_MAX / 2 || kv_len > INT32_MAX / 2 || n_corr > INT32_MAX / 2)
+    return "problem too large (row or key count beyond 2^30)";
+
+  p.kind = 0;
+  p.h_q = h_q; p.h_kv = h_kv; p.d = d;
+  p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  p.n_q = n_q;
+  p.n_seg[0] = kv_len;
+  p.n_seg[1] = n_corr;
+  p.rows.assign(n_q * 4, 0);
+  auto clamp_kv = [&](int64_t hi_global) {
+    return (int32_t)std::min<int64_t>(kv_len, std::max<int64_t>(0, hi_global - kv_off));
+  };
+  for (int64_t i = 0; i < q_len; ++i) {                  // clean rows: block-causal
+    int64_t pos = q_off + i;
+    int32_t hi = clamp_kv((pos / B + 1) * B);
+    p.rows[i * 4 + 1] = hi;
+  }
+  for (int64_t m = 0; m < n_owned; ++m) {                // corrupted rows: clean prefix + own block
+    int32_t hi = clamp_kv(owned[m] * B);
+    for (int64_t j = 0; j < B; ++j) {
+      int64_t r = q_len + m * B + j;
+      p.rows[r * 4 + 1] = hi;
+      if (local) {
+        p.rows[r * 4 + 2] = (int32_t)(m * B);
+        p.rows[r * 4 + 3] = (int32_t)((m + 1) * B);
+      }
+    }
+  }
+  tile_regions(p, {Region{0, q_len}, Region{q_len, n_q}});
+  finish(p);
+  return "";
+}
+
+std::string build_varlen(Plan &p, const int32_t *cu, int32_t n_seqs, bool causal, int32_t h_q,
+                         int32_t h_kv, int32_t d, float scale) {
+  if (!cu) return "cu_seqlens is NULL";
+  if (n_seqs < 0) return "n_seqs must be >= 0";
+  if (cu[0] != 0) return "cu_seqlens[0] must be 0";
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (cu[i + 1] < cu[i]) return "cu_seqlens must be non-decreasing";
+  std::string e = check_heads(h_q, h_kv, d);
+  if (!e.empty()) return e;
+  const int64_t T = cu[n_seqs];
+  if (T > INT32_MAX / 2) return "problem too large";
+  p.kind = 1;
+  p.h_q = h_q; p.h_kv = h_kv; p.d = d;
+  p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  p.n_q = T;
+  p.n_seg[0] = T;
+  p.n_seg[1] = 0;
+  p.rows.assign(T * 4, 0);
+  std::vector<Region> regions;
+  for (int32_t s = 0; s < n_seqs; ++s) {
+    for (int64_t r = cu[s]; r < cu[s + 1]; ++r) {
+      p.rows[r * 4 + 0] = cu[s];
+      p.rows[r * 4 + 1] = causal ? (int32_t)(r + 1) : cu[s + 1];
+    }
+    if (cu[s + 1] > cu[s]) regions.push_back(Region{cu[s], cu[s + 1]});
+  }
+  tile_regions(p, regions);
+  finish(p);
+  return "";
+}
+
+}  // namespace bdattn

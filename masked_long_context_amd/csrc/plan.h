@@ -1,0 +1,61 @@
+// Host-side block-sparse tile schedule (internal; host C++17 only).
+#pragma once
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tiling.h"
+
+namespace bdattn {
+
+// Per query tile: rows [q0, q0 + rows) and, for each key segment, the bounding
+// values of the rows' legal ranges [lo, hi):
+//   lo_min/hi_max bound the keys any row attends (non-empty rows only);
+//   lo_max/hi_min tell which key tiles need no mask: [k0, k1) is full for the
+//   tile iff lo_max <= k0 and k1 <= hi_min (an empty row forces hi_min = 0).
+struct SegSummary { int32_t lo_min, lo_max, hi_min, hi_max; };
+struct TileDesc { int32_t q0, rows; SegSummary seg[2]; int32_t cost, pad; };
+struct KTile { int32_t seg, k0, begin, end; };
+static_assert(sizeof(TileDesc) == 48, "TileDesc layout");
+static_assert(sizeof(KTile) == 16, "KTile layout");
+
+struct ImageHeader {
+  int32_t magic, n_q, n_fwd, n_bq, n_kt, n_list, n_seg0, n_seg1;
+  int64_t off_rows, off_fwd, off_bq, off_kt, off_list, image_bytes;
+};
+
+struct Plan {
+  uint64_t id = 0;
+  int kind = 0;                 // 0: BDLM rank share, 1: varlen packed shards
+  int32_t h_q = 0, h_kv = 0, d = 0;
+  float scale = 0.f;
+  int64_t n_q = 0;
+  int64_t n_seg[2] = {0, 0};    // keys of segment 0 (clean range / packed) and 1 (local corrupted)
+  std::vector<int32_t> rows;    // 4 per row: lo0, hi0, lo1, hi1
+  std::vector<TileDesc> fwd;    // forward items, longest first
+  std::vector<TileDesc> bq;     // backward query tiles (natural order)
+  std::vector<KTile> kt;        // backward key tiles, longest list first
+  std::vector<int32_t> list;    // q-tile index | full << 31, grouped per key tile
+  int64_t useful_pairs = 0;
+  // Device image of the tables (uploaded into the head of each workspace).
+  std::vector<uint8_t> image;
+  ImageHeader hdr{};
+  // Workspace and prepare-buffer layout.
+  int64_t ws_t_off[2] = {0, 0}, ws_bytes = 0;
+  int64_t kpad[2] = {0, 0};
+  int64_t prep_q_off = 0, prep_do_off = 0, prep_bytes = 0;
+  // Pinned copy of `image` for asynchronous uploads (made on first use).
+  void *pinned = nullptr;
+  bool used = false;
+};
+
+// Both return an empty string on success, else the reason for rejecting the input.
+std::string build_bdlm(Plan &p, int64_t clean_len, int32_t B, int64_t q_off, int64_t q_len,
+                       const int64_t *owned, int64_t n_owned, int64_t kv_off, int64_t kv_len,
+                       bool local, int32_t h_q, int32_t h_kv, int32_t d, float scale);
+std::string build_varlen(Plan &p, const int32_t *cu, int32_t n_seqs, bool causal, int32_t h_q,
+                         int32_t h_kv, int32_t d, float scale);
+
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace bdattn

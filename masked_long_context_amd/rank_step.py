@@ -1,0 +1,134 @@
+"""One rank's attention step under context-sharded block parallelism (CSBP).
+
+The rank holds its clean query rows, the corrupted blocks it owns and their
+local corrupted K/V, and sees the clean K/V as position shards ("Block
+Parallelism For Efficient Distributed Long-Context Diffusion Language Model
+Training", English abstract).  The step runs, on one HIP stream:
+
+    for each clean K/V shard s:  bdattn_fwd  -> partial (O_s, LSE_s)
+    bdattn_lse_merge             -> O, LSE
+    bdattn_bwd_prepare           -> delta, transposed Q/dO tiles
+    for each clean K/V shard s:  bdattn_bwd  -> dQ (accumulated), dK_s, dV_s
+    bdattn_dq_finalize           -> dQ (bf16)
+
+The local corrupted K/V join the call of one chosen shard.  Shards whose plan
+has no legal pair are left out of the forward and the merge (their partial
+would carry LSE = -inf everywhere); their backward still runs and writes zero
+gradients.  This module only sequences calls and owns buffers; every
+arithmetic step runs in libbdattn.so.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import bdattn as B
+
+
+class BdlmRankStep:
+    def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda",
+                 part_dtype=torch.float32, keep_partials: bool = False):
+        self.problem = problem
+        self.shards = list(shards)
+        self.device = device
+        self.plans: List[B.Plan] = [B.Plan.from_problem(problem.with_kv(o, n, loc)) for (o, n, loc) in shards]
+        self.active = [i for i, pl in enumerate(self.plans) if pl.useful_pairs > 0]
+        p = problem
+        self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
+        self.ws = B.workspace(max(pl.workspace_bytes for pl in self.plans), device)
+        self.prep = B.workspace(max(pl.prepare_bytes for pl in self.plans), device)
+        n_parts = max(1, len(self.active))
+        self.o_parts = torch.empty((n_parts, self.n_q, self.h_q, self.d), dtype=part_dtype, device=device)
+        self.lse_parts = torch.empty((n_parts, self.h_q, self.n_q), dtype=torch.float32, device=device)
+        self.o = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((self.h_q, self.n_q), dtype=torch.float32, device=device)
+        self.delta = torch.empty((self.h_q, self.n_q), dtype=torch.float32, device=device)
+        self.dq_acc = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.float32, device=device)
+        self.dq = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.bfloat16, device=device)
+        self.dk_clean = torch.empty((p.clean_len, self.h_kv, self.d), dtype=torch.bfloat16, device=device)
+        self.dv_clean = torch.empty_like(self.dk_clean)
+        self.dk_corr = torch.empty((p.n_corr, self.h_kv, self.d), dtype=torch.bfloat16, device=device)
+        self.dv_corr = torch.empty_like(self.dk_corr)
+        self.keep_partials = keep_partials
+        self.timer = None      # optional callable(tag) -> context manager around each library call
+
+    @property
+    def useful_pairs(self) -> int:
+        """Legal pairs per q-head over the whole step (all shards)."""
+        return sum(pl.useful_pairs for pl in self.plans)
+
+    def _t(self, tag):
+        import contextlib
+        return self.timer(tag) if self.timer is not None else contextlib.nullcontext()
+
+    def forward(self, q, k_clean, v_clean, k_corr, v_corr):
+        if not self.active:
+            self.o.zero_()
+            self.lse.fill_(float("-inf"))
+            return self.o, self.lse
+        for slot, i in enumerate(self.active):
+            off, n, local = self.shards[i]
+            with self._t("fwd"):
+                B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
+                             k_corr if local else None, v_corr if local else None,
+                             self.o_parts[slot], self.lse_parts[slot], self.ws)
+        with self._t("merge"):
+            B.bdattn_lse_merge(self.o_parts[:len(self.active)], self.lse_parts[:len(self.active)],
+                               self.o, self.lse)
+        return self.o, self.lse
+
+    def backward(self, q, k_clean, v_clean, k_corr, v_corr, dout):
+        with self._t("prepare"):
+            B.bdattn_bwd_prepare(self.plans[0], q, self.o, dout, self.delta, self.dq_acc, self.prep)
+        for i, (off, n, local) in enumerate(self.shards):
+            with self._t("bwd"):
+                B.bdattn_bwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
+                             k_corr if local else None, v_corr if local else None, dout, self.lse,
+                             self.delta, self.prep, self.dq_acc, self.dk_clean[off:off + n],
+                             self.dv_clean[off:off + n], self.dk_corr if local else None,
+                             self.dv_corr if local else None, self.ws)
+        with self._t("finalize"):
+            B.bdattn_dq_finalize(self.dq_acc, self.dq)
+        return self.dq, self.dk_clean, self.dv_clean, self.dk_corr, self.dv_corr
+
+    def step(self, q, k_clean, v_clean, k_corr, v_corr, dout):
+        self.forward(q, k_clean, v_clean, k_corr, v_corr)
+        return self.backward(q, k_clean, v_clean, k_corr, v_corr, dout)
+
+
+class VarlenStep:
+    """Forward + backward of packed independent shards (one call each)."""
+
+    def __init__(self, cu_seqlens, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0):
+        self.plan = B.Plan.varlen(cu_seqlens, causal, h_q, h_kv, head_dim, softmax_scale)
+        T = int(cu_seqlens[-1])
+        self.T, self.h_q, self.h_kv, self.d = T, h_q, h_kv, head_dim
+        self.ws = B.workspace(self.plan.workspace_bytes, device)
+        self.prep = B.workspace(self.plan.prepare_bytes, device)
+        self.o = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((h_q, T), dtype=torch.float32, device=device)
+        self.delta = torch.empty((h_q, T), dtype=torch.float32, device=device)
+        self.dq_acc = torch.empty((T, h_q, head_dim), dtype=torch.float32, device=device)
+        self.dq = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
+        self.dk = torch.empty((T, h_kv, head_dim), dtype=torch.bfloat16, device=device)
+        self.dv = torch.empty_like(self.dk)
+
+    @property
+    def useful_pairs(self) -> int:
+        return self.plan.useful_pairs
+
+    def forward(self, q, k, v):
+        B.bdattn_varlen_fwd(self.plan, q, k, v, self.o, self.lse, self.ws)
+        return self.o, self.lse
+
+    def backward(self, q, k, v, dout):
+        B.bdattn_bwd_prepare(self.plan, q, self.o, dout, self.delta, self.dq_acc, self.prep)
+        B.bdattn_varlen_bwd(self.plan, q, k, v, dout, self.lse, self.delta, self.prep, self.dq_acc,
+                            self.dk, self.dv, self.ws)
+        B.bdattn_dq_finalize(self.dq_acc, self.dq)
+        return self.dq, self.dk, self.dv
+
+    def step(self, q, k, v, dout):
+        self.forward(q, k, v)
+        return self.backward(q, k, v, dout)

@@ -1,0 +1,159 @@
+"""Host tile scheduler against the oracle's explicit mask (CPU only).
+
+Checks that the per-row key ranges equal the mask, that the scheduled tiles
+cover every legal pair, that tiles marked full hold no masked pair, that no
+scheduled tile is empty, the useful-pair counts (closed forms of the
+workloads), and the longest-first ordering."""
+import numpy as np
+import pytest
+
+import oracle
+from masked_long_context_amd import bdattn as B
+from masked_long_context_amd import workloads as wl
+
+FWD_BN, BWD_BN = 64, 128
+
+
+def _mask_and_plan(p):
+    plan = B.Plan.from_problem(p)
+    m = oracle.bdlm_mask(p.clean_len, p.block_size, p.q_clean_offset, p.q_clean_len, p.owned_blocks,
+                         p.kv_clean_offset, p.kv_clean_len, p.with_local_corrupt)
+    return plan, m
+
+
+def _check_plan(plan, m, n0, n1):
+    rows = plan.export(0)
+    nq = m.shape[0]
+    assert rows.shape == (nq, 4)
+    # 1. per-row ranges reproduce the mask exactly
+    rebuilt = np.zeros_like(m)
+    for r in range(nq):
+        lo0, hi0, lo1, hi1 = rows[r]
+        if hi0 > lo0:
+            rebuilt[r, lo0:hi0] = True
+        if hi1 > lo1:
+            rebuilt[r, n0 + lo1:n0 + hi1] = True
+    assert np.array_equal(rebuilt, m)
+    assert plan.useful_pairs == int(m.sum())
+
+    def seg_cols(s, k0, k1):
+        base = 0 if s == 0 else n0
+        n = n0 if s == 0 else n1
+        return base + k0, base + min(k1, n)
+
+    # 2. forward items: every row once; visited tiles cover the mask; full tiles are all legal
+    items = plan.export(1)
+    seen = np.zeros(nq, int)
+    covered = np.zeros_like(m)
+    costs = []
+    for it in items:
+        q0, nr = it[0], it[1]
+        seen[q0:q0 + nr] += 1
+        costs.append(it[10])
+        for s in range(2):
+            lo_min, lo_max, hi_min, hi_max = it[2 + 4 * s: 6 + 4 * s]
+            if hi_max <= lo_min:
+                assert not m[q0:q0 + nr, seg_cols(s, 0, n0 if s == 0 else n1)[0]:
+                             seg_cols(s, 0, n0 if s == 0 else n1)[1]].any()
+                continue
+            for k0 in range(lo_min // FWD_BN * FWD_BN, hi_max, FWD_BN):
+                a, b = seg_cols(s, k0, k0 + FWD_BN)
+                covered[q0:q0 + nr, a:b] = True
+                full = lo_max <= k0 and k0 + FWD_BN <= hi_min
+                if full:
+                    assert m[q0:q0 + nr, a:b].all()
+                    assert b - a == FWD_BN
+    assert np.all(seen == 1)
+    assert not (m & ~covered).any()
+    assert costs == sorted(costs, reverse=True)
+
+    # 3. backward: k-tiles cover every key once, lists cover the mask, full entries all legal,
+    #    no entry without a legal pair, longest list first
+    bq = plan.export(2)
+    kts = plan.export(3)
+    lst = plan.export(4)
+    cov_b = np.zeros_like(m)
+    keys_seen = {0: set(), 1: set()}
+    lens = []
+    for s, k0, beg, end in kts:
+        keys_seen[s].add(k0)
+        lens.append(end - beg)
+        a, b = seg_cols(s, k0, k0 + BWD_BN)
+        for e in lst[beg:end]:
+            full = e < 0
+            qi = e & 0x7FFFFFFF
+            q0, nr = bq[qi][0], bq[qi][1]
+            blk = m[q0:q0 + nr, a:b]
+            assert blk.any()
+            cov_b[q0:q0 + nr, a:b] = True
+            if full:
+                assert blk.all() and b - a == BWD_BN
+    assert keys_seen[0] == set(range(0, n0, BWD_BN))
+    assert keys_seen[1] == set(range(0, n1, BWD_BN))
+    assert not (m & ~cov_b).any()
+    assert lens == sorted(lens, reverse=True)
+    # backward q-tiles cover every row once
+    seen = np.zeros(nq, int)
+    for t in bq:
+        seen[t[0]:t[0] + t[1]] += 1
+    assert np.all(seen == 1)
+
+
+SMALL = [
+    wl.small_bdlm_config(512, 16, 4, 1, 4, 2, 128, 4),
+    wl.small_bdlm_config(768, 32, 2, 1, 2, 1, 64, 3),
+    wl.small_bdlm_config(384, 24, 2, 0, 2, 2, 128, 2),
+    wl.small_bdlm_config(64, 1, 2, 1, 1, 1, 64, 2),
+    wl.small_bdlm_config(1024, 128, 2, 1, 2, 1, 128, 2),
+    wl.small_bdlm_config(1600, 200, 2, 1, 2, 2, 64, 4),
+    wl.config(1),
+    wl.config(2),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_bdlm_plans_match_mask(cfg):
+    total = 0
+    for p in cfg.shard_problems() + [cfg.problem]:
+        plan, m = _mask_and_plan(p)
+        _check_plan(plan, m, p.kv_clean_len, p.n_corr if p.with_local_corrupt else 0)
+    for p in cfg.shard_problems():
+        total += B.Plan.from_problem(p).useful_pairs
+    assert total == B.Plan.from_problem(cfg.problem).useful_pairs
+
+
+def test_random_bdlm_plans_match_mask():
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        Bs = int(rng.choice([1, 2, 5, 16, 32, 48]))
+        nb = int(rng.integers(2, 12))
+        L = nb * Bs
+        q0 = int(rng.integers(0, nb)) * Bs
+        ql = int(rng.integers(0, nb - q0 // Bs + 1)) * Bs
+        owned = [int(x) for x in rng.permutation(nb)[:int(rng.integers(0, nb + 1))]]
+        k0 = int(rng.integers(0, nb)) * Bs
+        kl = int(rng.integers(0, nb - k0 // Bs + 1)) * Bs
+        local = bool(rng.integers(0, 2))
+        p = wl.BdlmProblem(L, Bs, q0, ql, tuple(owned), k0, kl, local, 2, 1, 64)
+        plan, m = _mask_and_plan(p)
+        _check_plan(plan, m, kl, p.n_corr if local else 0)
+
+
+@pytest.mark.parametrize("lens,causal", [([1, 5, 130, 64, 257, 300], True), ([7, 129, 128, 1], False),
+                                         ([0, 70, 0, 200], True)])
+def test_varlen_plans_match_mask(lens, causal):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    plan = B.Plan.varlen(cu, causal, 4, 2, 128)
+    m = oracle.varlen_mask(cu, causal)
+    _check_plan(plan, m, int(cu[-1]), 0)
+
+
+@pytest.mark.parametrize("idx,expected", [(1, 73728), (2, 17039360), (3, 4429709312), (5, 146030985216)])
+def test_useful_pairs_of_workloads(idx, expected):
+    cfg = wl.config(idx)
+    assert sum(B.Plan.from_problem(p).useful_pairs for p in cfg.shard_problems()) == expected
+
+
+def test_varlen_workload_pairs():
+    cfg = wl.config(4)
+    assert B.Plan.varlen(cfg.cu_seqlens, True, 32, 8, 128).useful_pairs == 3214974270
