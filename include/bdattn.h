@@ -41,8 +41,8 @@
  *   packed varlen Q/O/dO  [total][h_q][head_dim], K/V [total][h_kv][head_dim]
  * Tensors are bf16 unless stated.  Device pointers must be 16-byte aligned.
  *
- * Ownership.  Every device buffer, including the workspace and the prepare
- * buffer, belongs to the caller; the library never allocates device memory.
+ * Ownership.  Every device buffer, including the workspace, belongs to the
+ * caller; the library never allocates device memory.
  * A plan holds host memory only (plus a pinned host copy of its tables, made
  * on first use); it is immutable and may be shared between threads.  A plan
  * must not be destroyed while work enqueued with it may still run
@@ -70,7 +70,7 @@ typedef enum {
   BDATTN_EINVAL = -1,        /* null pointer, negative size, bad head counts ...            */
   BDATTN_EALIGN = -2,        /* offsets/lengths not multiples of block_size, misaligned ptr */
   BDATTN_EUNSUPPORTED = -3,  /* head_dim not in {64, 128}, dtype not supported            */
-  BDATTN_EWORKSPACE = -4,    /* workspace / prepare buffer too small                       */
+  BDATTN_EWORKSPACE = -4,    /* workspace too small                                         */
   BDATTN_EHIP = -5           /* a HIP runtime call failed                                   */
 } bdattn_status;
 
@@ -110,9 +110,8 @@ int bdattn_plan_create_varlen(const int32_t *cu_seqlens, int32_t n_seqs, int32_t
 
 void bdattn_plan_destroy(bdattn_plan *plan);
 
-/* Sizes (bytes) of the per-call workspace and of the backward prepare buffer. */
+/* Size (bytes) of the per-call workspace: the plan's tables, uploaded by each call. */
 int64_t bdattn_plan_workspace_bytes(const bdattn_plan *plan);
-int64_t bdattn_plan_prepare_bytes(const bdattn_plan *plan);
 /* Legal (query, key) pairs per query head: the useful-work count. */
 int64_t bdattn_plan_useful_pairs(const bdattn_plan *plan);
 /* Query rows, and key rows of the clean (or packed) range and of the local corrupted K/V. */
@@ -150,26 +149,26 @@ int bdattn_lse_merge(int32_t n_parts, const void *o_parts, int32_t part_dtype, c
                      float *lse_out, void *stream);
 
 /* Backward preparation, once per rank step (shared by every K/V range):
- * delta[h][r] = sum_d dO[r][h][d] * O[r][h][d] from the MERGED output O (o_dtype),
- * and the transposed query-side tiles the backward reads, into `prepare`
- * (>= bdattn_plan_prepare_bytes); when dq_accum is not NULL it is also cleared
- * to 0 (fp32 [n_q][h_q][d]).  Any plan of the same query side (same clean query
- * rows and owned blocks) may be used; the backward reads the tiles by index. */
-int bdattn_bwd_prepare(const bdattn_plan *plan, const void *q, const void *o, int32_t o_dtype,
-                       const void *dout, float *delta, float *dq_accum, void *prepare,
-                       int64_t prepare_bytes, void *stream);
+ * delta[h][r] = sum_d dO[r][h][d] * O[r][h][d] (fp32 [h_q][n_q]) from the MERGED
+ * output O (o_dtype), and, when dq_accum is not NULL, dq_accum (fp32
+ * [n_q][h_q][d]) cleared to 0.  Only the plan's query side (n_q, h_q, head_dim)
+ * is used. */
+int bdattn_bwd_prepare(const bdattn_plan *plan, const void *o, int32_t o_dtype, const void *dout,
+                       float *delta, float *dq_accum, void *stream);
 
-/* Backward of one K/V range given the MERGED lse and the prepared delta/tiles:
- *   P = exp(S - LSE), dS = P o (dO V^T - delta)
- *   dq_accum += scale dS K    (fp32 [n_q][h_q][d], accumulated with atomics across calls)
- *   dk = scale dS^T Q, dv = P^T dO, summed over the q-heads of each KV head, written with `=`
- *   (bf16) for every key of the range, zeros for keys no query attends.
- * dk_corr/dv_corr may be NULL when the plan has no local corrupted keys. */
+/* Backward of one K/V range given the MERGED lse and the prepared delta:
+ *   P = exp(scale Q K^T - LSE) on the legal pairs, dS = P o (dO V^T - delta)
+ *   dq_accum += scale dS K    (fp32 [n_q][h_q][d]; each call adds its range)
+ *   dk = scale dS^T Q, dv = P^T dO, summed over the q-heads of each KV head and
+ *   written with `=` (bf16) for every key of the range (zeros for keys no query
+ *   attends).
+ * Two kernels run in order on `stream`: a key-major one for dK/dV and a
+ * query-major one for dQ.  dk_corr/dv_corr may be NULL when the plan has no
+ * local corrupted keys.  workspace: >= bdattn_plan_workspace_bytes. */
 int bdattn_bwd(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
                const void *k_corr, const void *v_corr, const void *dout, const float *lse,
-               const float *delta, const void *prepare, int64_t prepare_bytes, float *dq_accum,
-               void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr, void *workspace,
-               int64_t workspace_bytes, void *stream);
+               const float *delta, float *dq_accum, void *dk_clean, void *dv_clean, void *dk_corr,
+               void *dv_corr, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* dq (bf16) = dq_accum (fp32), n_elems elements. */
 int bdattn_dq_finalize(const float *dq_accum, void *dq, int64_t n_elems, void *stream);
@@ -179,9 +178,8 @@ int bdattn_varlen_fwd(const bdattn_plan *plan, const void *q, const void *k, con
                       int32_t o_dtype, float *lse, void *workspace, int64_t workspace_bytes,
                       void *stream);
 int bdattn_varlen_bwd(const bdattn_plan *plan, const void *q, const void *k, const void *v,
-                      const void *dout, const float *lse, const float *delta, const void *prepare,
-                      int64_t prepare_bytes, float *dq_accum, void *dk, void *dv, void *workspace,
-                      int64_t workspace_bytes, void *stream);
+                      const void *dout, const float *lse, const float *delta, float *dq_accum,
+                      void *dk, void *dv, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Thread-local message describing the last non-OK status on this thread. */
 const char *bdattn_last_error(void);

@@ -45,7 +45,6 @@ _SIGS = {
                                             c_int32, c_float, ctypes.POINTER(c_void_p)]),
     "bdattn_plan_destroy": (None, [c_void_p]),
     "bdattn_plan_workspace_bytes": (c_int64, [c_void_p]),
-    "bdattn_plan_prepare_bytes": (c_int64, [c_void_p]),
     "bdattn_plan_useful_pairs": (c_int64, [c_void_p]),
     "bdattn_plan_n_q": (c_int64, [c_void_p]),
     "bdattn_plan_n_kv": (c_int64, [c_void_p, c_int32]),
@@ -53,12 +52,11 @@ _SIGS = {
     "bdattn_fwd": (c_int32, [c_void_p] * 7 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_lse_merge": (c_int32, [c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_int32, c_void_p,
                                    c_int32, c_void_p, c_void_p]),
-    "bdattn_bwd_prepare": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_int64, c_void_p]),
-    "bdattn_bwd": (c_int32, [c_void_p] * 10 + [c_int64] + [c_void_p] * 6 + [c_int64, c_void_p]),
+    "bdattn_bwd_prepare": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "bdattn_bwd": (c_int32, [c_void_p] * 15 + [c_int64, c_void_p]),
     "bdattn_dq_finalize": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_fwd": (c_int32, [c_void_p] * 5 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
-    "bdattn_varlen_bwd": (c_int32, [c_void_p] * 8 + [c_int64] + [c_void_p] * 4 + [c_int64, c_void_p]),
+    "bdattn_varlen_bwd": (c_int32, [c_void_p] * 11 + [c_int64, c_void_p]),
     "bdattn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -149,10 +147,6 @@ class Plan:
         return lib().bdattn_plan_workspace_bytes(self._h)
 
     @property
-    def prepare_bytes(self) -> int:
-        return lib().bdattn_plan_prepare_bytes(self._h)
-
-    @property
     def useful_pairs(self) -> int:
         return lib().bdattn_plan_useful_pairs(self._h)
 
@@ -208,23 +202,21 @@ def bdattn_lse_merge(o_parts, lse_parts, o_out, lse_out, stream=None):
                                   _ptr(o_out), _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
 
 
-def bdattn_bwd_prepare(plan: Plan, q, o, dout, delta, dq_accum, prep, stream=None):
-    _check(lib().bdattn_bwd_prepare(plan.handle, _ptr(q), _ptr(o), _dtype_code(o), _ptr(dout), _ptr(delta),
-                                    _ptr(dq_accum), _ptr(prep), prep.numel(), _stream(stream)))
+def bdattn_bwd_prepare(plan: Plan, o, dout, delta, dq_accum=None, stream=None):
+    _check(lib().bdattn_bwd_prepare(plan.handle, _ptr(o), _dtype_code(o), _ptr(dout), _ptr(delta),
+                                    _ptr(dq_accum), _stream(stream)))
 
 
-def bdattn_bwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, prep, dq_accum,
+def bdattn_bwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq_accum,
                dk_clean, dv_clean, dk_corr, dv_corr, ws, stream=None):
     _check(lib().bdattn_bwd(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
-                            _ptr(dout), _ptr(lse), _ptr(delta), _ptr(prep), prep.numel(), _ptr(dq_accum),
-                            _ptr(dk_clean), _ptr(dv_clean), _ptr(dk_corr), _ptr(dv_corr), _ptr(ws), ws.numel(),
-                            _stream(stream)))
+                            _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(dk_clean), _ptr(dv_clean),
+                            _ptr(dk_corr), _ptr(dv_corr), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def bdattn_varlen_bwd(plan: Plan, q, k, v, dout, lse, delta, prep, dq_accum, dk, dv, ws, stream=None):
+def bdattn_varlen_bwd(plan: Plan, q, k, v, dout, lse, delta, dq_accum, dk, dv, ws, stream=None):
     _check(lib().bdattn_varlen_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
-                                   _ptr(prep), prep.numel(), _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(ws),
-                                   ws.numel(), _stream(stream)))
+                                   _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def bdattn_dq_finalize(dq_accum, dq, stream=None):

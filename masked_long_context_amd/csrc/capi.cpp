@@ -111,16 +111,13 @@ int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   hipStream_t s = (hipStream_t)stream;
   rc = upload(pl, ws, s);
   if (rc != BDATTN_OK) return rc;
-  const void *kk[2] = {k0, k1}, *vv[2] = {v0, v1};
   bdattn::FwdArgs a{};
-  for (int g = 0; g < 2; ++g) {
-    void *t = (char *)ws + p.ws_t_off[g];
-    if (p.n_seg[g] > 0) HIP_CHECK(bdattn::launch_transpose(vv[g], p.n_seg[g], p.h_kv, p.d, p.kpad[g], true, t, s), "transpose V");
-    a.k[g] = kk[g];
-    a.vt[g] = t;
-    a.kpad[g] = p.kpad[g];
-    a.n_seg[g] = (int32_t)p.n_seg[g];
-  }
+  a.k[0] = k0;
+  a.k[1] = k1;
+  a.v[0] = v0;
+  a.v[1] = v1;
+  a.n_seg[0] = (int32_t)p.n_seg[0];
+  a.n_seg[1] = (int32_t)p.n_seg[1];
   a.q = q;
   a.o = o;
   a.lse = lse;
@@ -138,9 +135,8 @@ int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
 }
 
 int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
-            const void *v1, const void *dout, const float *lse, const float *delta, const void *prep,
-            int64_t prep_bytes, float *dq, void *dk0, void *dv0, void *dk1, void *dv1, void *ws,
-            int64_t ws_bytes, void *stream) {
+            const void *v1, const void *dout, const float *lse, const float *delta, float *dq, void *dk0,
+            void *dv0, void *dk1, void *dv1, void *ws, int64_t ws_bytes, void *stream) {
   bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
   const bdattn::Plan &p = pl->p;
   const bool rows = p.n_q > 0;
@@ -159,43 +155,34 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   CHECK_PTR(v1, p.n_seg[1] > 0);
   CHECK_PTR(dk1, p.n_seg[1] > 0);
   CHECK_PTR(dv1, p.n_seg[1] > 0);
-  if (work) {
-    CHECK(prep != nullptr, BDATTN_EINVAL, "prepare buffer is NULL");
-    CHECK(aligned(prep, BDATTN_ALIGN), BDATTN_EALIGN, "prepare buffer is not 256-byte aligned");
-    CHECK(prep_bytes >= p.prep_bytes, BDATTN_EWORKSPACE,
-          "prepare buffer too small: need " + std::to_string(p.prep_bytes) + " bytes");
-  }
   int rc = check_ws(p, ws, ws_bytes);
   if (rc != BDATTN_OK) return rc;
   if (!any_keys) return BDATTN_OK;
   hipStream_t s = (hipStream_t)stream;
   rc = upload(pl, ws, s);
   if (rc != BDATTN_OK) return rc;
-  const void *kk[2] = {k0, k1}, *vv[2] = {v0, v1};
-  void *dk[2] = {dk0, dk1}, *dv[2] = {dv0, dv1};
   bdattn::BwdArgs a{};
-  for (int g = 0; g < 2; ++g) {
-    void *t = (char *)ws + p.ws_t_off[g];
-    if (p.n_seg[g] > 0) HIP_CHECK(bdattn::launch_transpose(kk[g], p.n_seg[g], p.h_kv, p.d, p.kpad[g], false, t, s), "transpose K");
-    a.k[g] = kk[g];
-    a.v[g] = vv[g];
-    a.kt[g] = t;
-    a.kpad[g] = p.kpad[g];
-    a.n_seg[g] = (int32_t)p.n_seg[g];
-    a.dk[g] = dk[g];
-    a.dv[g] = dv[g];
-  }
+  a.k[0] = k0;
+  a.k[1] = k1;
+  a.v[0] = v0;
+  a.v[1] = v1;
+  a.dk[0] = dk0;
+  a.dk[1] = dk1;
+  a.dv[0] = dv0;
+  a.dv[1] = dv1;
+  a.n_seg[0] = (int32_t)p.n_seg[0];
+  a.n_seg[1] = (int32_t)p.n_seg[1];
   a.q = q;
   a.dout = dout;
-  a.qt = (const char *)prep + p.prep_q_off;
-  a.dot = (const char *)prep + p.prep_do_off;
   a.lse = lse;
   a.delta = delta;
   a.dq = dq;
   a.rows = img(ws, p.hdr.off_rows);
+  a.items = img(ws, p.hdr.off_fwd);
   a.bq = img(ws, p.hdr.off_bq);
   a.ktiles = img(ws, p.hdr.off_kt);
   a.list = img(ws, p.hdr.off_list);
+  a.n_items = rows ? p.hdr.n_fwd : 0;
   a.n_kt = p.hdr.n_kt;
   a.n_bq = p.hdr.n_bq;
   a.n_q = (int32_t)p.n_q;
@@ -204,7 +191,7 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   a.group = p.h_q / p.h_kv;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
-  HIP_CHECK(bdattn::launch_bwd(a, p.d, s), "backward kernel");
+  HIP_CHECK(bdattn::launch_bwd(a, p.d, s), "backward kernels");
   return BDATTN_OK;
 }
 
@@ -264,9 +251,6 @@ void bdattn_plan_destroy(bdattn_plan *pl) {
 }
 
 int64_t bdattn_plan_workspace_bytes(const bdattn_plan *pl) { return pl ? pl->p.ws_bytes : BDATTN_EINVAL; }
-int64_t bdattn_plan_prepare_bytes(const bdattn_plan *pl) {
-  return pl ? pl->p.prep_bytes + (int64_t)pl->p.image.size() : BDATTN_EINVAL;
-}
 int64_t bdattn_plan_useful_pairs(const bdattn_plan *pl) { return pl ? pl->p.useful_pairs : BDATTN_EINVAL; }
 int64_t bdattn_plan_n_q(const bdattn_plan *pl) { return pl ? pl->p.n_q : BDATTN_EINVAL; }
 int64_t bdattn_plan_n_kv(const bdattn_plan *pl, int32_t seg) {
@@ -306,59 +290,44 @@ int bdattn_varlen_fwd(const bdattn_plan *pl, const void *q, const void *k, const
 }
 
 int bdattn_bwd(const bdattn_plan *pl, const void *q, const void *k_clean, const void *v_clean, const void *k_corr,
-               const void *v_corr, const void *dout, const float *lse, const float *delta, const void *prep,
-               int64_t prep_bytes, float *dq, void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr,
-               void *ws, int64_t ws_bytes, void *stream) {
+               const void *v_corr, const void *dout, const float *lse, const float *delta, float *dq,
+               void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr, void *ws, int64_t ws_bytes,
+               void *stream) {
   if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
   if (pl->p.kind != 0) return fail(BDATTN_EINVAL, "plan is a varlen plan; use bdattn_varlen_bwd");
-  return run_bwd(pl, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, prep, prep_bytes, dq, dk_clean,
-                 dv_clean, dk_corr, dv_corr, ws, ws_bytes, stream);
+  return run_bwd(pl, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq, dk_clean, dv_clean, dk_corr,
+                 dv_corr, ws, ws_bytes, stream);
 }
 
 int bdattn_varlen_bwd(const bdattn_plan *pl, const void *q, const void *k, const void *v, const void *dout,
-                      const float *lse, const float *delta, const void *prep, int64_t prep_bytes, float *dq,
-                      void *dk, void *dv, void *ws, int64_t ws_bytes, void *stream) {
+                      const float *lse, const float *delta, float *dq, void *dk, void *dv, void *ws,
+                      int64_t ws_bytes, void *stream) {
   if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
   if (pl->p.kind != 1) return fail(BDATTN_EINVAL, "plan is not a varlen plan; use bdattn_bwd");
-  return run_bwd(pl, q, k, v, nullptr, nullptr, dout, lse, delta, prep, prep_bytes, dq, dk, dv, nullptr, nullptr,
-                 ws, ws_bytes, stream);
+  return run_bwd(pl, q, k, v, nullptr, nullptr, dout, lse, delta, dq, dk, dv, nullptr, nullptr, ws, ws_bytes,
+                 stream);
 }
 
-int bdattn_bwd_prepare(const bdattn_plan *cpl, const void *q, const void *o, int32_t o_dtype, const void *dout,
-                       float *delta, float *dq_accum, void *prep, int64_t prep_bytes, void *stream) {
-  if (!cpl) return fail(BDATTN_EINVAL, "plan is NULL");
-  bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
+int bdattn_bwd_prepare(const bdattn_plan *pl, const void *o, int32_t o_dtype, const void *dout, float *delta,
+                       float *dq_accum, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
   const bdattn::Plan &p = pl->p;
   CHECK(o_dtype == BDATTN_BF16 || o_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "o_dtype must be BF16 or F32");
   const bool rows = p.n_q > 0;
-  CHECK_PTR(q, rows);
   CHECK_PTR(o, rows);
   CHECK_PTR(dout, rows);
   CHECK_PTR(delta, rows);
   if (dq_accum) CHECK_PTR(dq_accum, rows);
-  CHECK(prep != nullptr, BDATTN_EINVAL, "prepare buffer is NULL");
-  CHECK(aligned(prep, BDATTN_ALIGN), BDATTN_EALIGN, "prepare buffer is not 256-byte aligned");
-  const int64_t need = p.prep_bytes + (int64_t)p.image.size();
-  CHECK(prep_bytes >= need, BDATTN_EWORKSPACE, "prepare buffer too small: need " + std::to_string(need) + " bytes");
   if (!rows) return BDATTN_OK;
-  hipStream_t s = (hipStream_t)stream;
-  char *table = (char *)prep + p.prep_bytes;    // tables after the slabs
-  int rc = upload(pl, table, s);
-  if (rc != BDATTN_OK) return rc;
   bdattn::PrepArgs a{};
-  a.q = q;
   a.o = o;
   a.dout = dout;
   a.o_f32 = o_dtype == BDATTN_F32;
   a.delta = delta;
   a.dq_zero = dq_accum;
-  a.qt = (char *)prep + p.prep_q_off;
-  a.dot = (char *)prep + p.prep_do_off;
-  a.bq = img(table, p.hdr.off_bq);
-  a.n_bq = p.hdr.n_bq;
   a.n_q = (int32_t)p.n_q;
   a.h_q = p.h_q;
-  HIP_CHECK(bdattn::launch_prepare(a, p.d, s), "prepare kernel");
+  HIP_CHECK(bdattn::launch_prepare(a, p.d, (hipStream_t)stream), "prepare kernel");
   return BDATTN_OK;
 }
 

@@ -1,6 +1,5 @@
 // Bandwidth-bound companions of the attention kernels on gfx950:
-//   transpose  K or V [n][h_kv][d] -> [h_kv][d][kpad] (MFMA operand copies)
-//   prepare    delta = rowsum(dO o O) and transposed Q / dO slabs per query tile
+//   prepare    delta = rowsum(dO o O) (and a clear of the dQ accumulator)
 //   merge      exact log-sum-exp merge of per-range partials
 //   finalize   fp32 dQ accumulator -> bf16
 #include "common.h"
@@ -9,93 +8,38 @@
 namespace bdattn {
 namespace {
 
-// One block = 64 keys of one KV head.  permute: store each 16-key chunk in the
-// order a 32x32 MFMA's C registers hold it (see perm16).
-template <int D>
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, int64_t n, int h_kv, int64_t kpad,
-                                                         int permute, bf16 *out) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[D][64 + 8];
-  const int tid = threadIdx.x;
-  const int kvh = blockIdx.y;
-  const int64_t key0 = (int64_t)blockIdx.x * 64;
-  for (int c = tid; c < 64 * D / 8; c += 256) {
-    const int r = c / (D / 8), col = c % (D / 8);
-    const int64_t key = key0 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < n) v = ld_u32x4(x + (key * h_kv + kvh) * D + col * 8);
-    const bf16x8 b = __builtin_bit_cast(bf16x8, v);
-    const int pos = permute ? ((r & ~15) | perm16(r & 15)) : r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[col * 8 + e][pos] = b[e];
-  }
-  __syncthreads();
-  for (int c = tid; c < D * 8; c += 256) {
-    const int d = c / 8, col = c % 8;
-    st_u32x4(out + ((int64_t)kvh * D + d) * kpad + key0 + col * 8, ld_u32x4(&tile[d][col * 8]));
-  }
-}
-
-// One block = one backward query tile (BWD_BM rows) of one q-head.
+// delta[h][r] = <dO[r][h], O[r][h]> (fp32), and the optional clear of the dQ
+// accumulator.  D/8 threads per (row, head), each on 8 consecutive elements.
 template <int D>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
-  constexpr int BM = BDATTN_BWD_BM;
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) bf16 tq[D][BM + 8];
-  __shared__ __attribute__((aligned(16))) bf16 tdo[D][BM + 8];
-  __shared__ float part[BM][CPR + 1];
-  const int tid = threadIdx.x;
-  const int qti = blockIdx.x, h = blockIdx.y;
-  const int q0 = a.bq[(int64_t)qti * 12], nrows = a.bq[(int64_t)qti * 12 + 1];
-  for (int c = tid; c < BM * CPR; c += 256) {
-    const int r = c / CPR, col = c % CPR;
-    u32x4 vq = {0u, 0u, 0u, 0u}, vd = vq;
-    float dot = 0.f;
-    if (r < nrows) {
-      const int64_t off = ((int64_t)(q0 + r) * a.h_q + h) * D + col * 8;
-      vq = ld_u32x4((const bf16 *)a.q + off);
-      vd = ld_u32x4((const bf16 *)a.dout + off);
-      const bf16x8 db = __builtin_bit_cast(bf16x8, vd);
-      if (a.o_f32) {
-        const f32x4 o0 = *reinterpret_cast<const f32x4 *>((const float *)a.o + off);
-        const f32x4 o1 = *reinterpret_cast<const f32x4 *>((const float *)a.o + off + 4);
+  constexpr int TPR = D / 8;
+  const int tid = threadIdx.x, h = blockIdx.y;
+  const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + tid / TPR;
+  const int sub = tid % TPR;
+  float dot = 0.f;
+  const bool valid = r < a.n_q;
+  const int64_t off = (r * a.h_q + h) * D + sub * 8;
+  if (valid) {
+    const bf16x8 db = ld_bf16x8((const bf16 *)a.dout + off);
+    if (a.o_f32) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4 *>((const float *)a.o + off);
+      const f32x4 o1 = *reinterpret_cast<const f32x4 *>((const float *)a.o + off + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot += (float)db[e] * o0[e] + (float)db[e + 4] * o1[e];
-      } else {
-        const bf16x8 ob = ld_bf16x8((const bf16 *)a.o + off);
+      for (int e = 0; e < 4; ++e) dot += (float)db[e] * o0[e] + (float)db[e + 4] * o1[e];
+    } else {
+      const bf16x8 ob = ld_bf16x8((const bf16 *)a.o + off);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot += (float)db[e] * (float)ob[e];
-      }
+      for (int e = 0; e < 8; ++e) dot += (float)db[e] * (float)ob[e];
     }
-    part[r][col] = dot;
-    const bf16x8 qb = __builtin_bit_cast(bf16x8, vq);
-    const bf16x8 db = __builtin_bit_cast(bf16x8, vd);
-    const int pos = (r & ~15) | perm16(r & 15);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      tq[col * 8 + e][pos] = qb[e];
-      tdo[col * 8 + e][pos] = db[e];
+    if (a.dq_zero) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4 *>(a.dq_zero + off) = z;
+      *reinterpret_cast<f32x4 *>(a.dq_zero + off + 4) = z;
     }
   }
-  __syncthreads();
-  if (tid < nrows) {
-    float acc = 0.f;
 #pragma unroll
-    for (int col = 0; col < CPR; ++col) acc += part[tid][col];
-    a.delta[(int64_t)h * a.n_q + q0 + tid] = acc;
-  }
-  if (a.dq_zero) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int c = tid; c < nrows * (D / 4); c += 256) {
-      const int r = c / (D / 4), col = c % (D / 4);
-      *reinterpret_cast<f32x4 *>(a.dq_zero + ((int64_t)(q0 + r) * a.h_q + h) * D + col * 4) = z;
-    }
-  }
-  const int64_t slab = ((int64_t)qti * a.h_q + h) * D * BM;
-  for (int c = tid; c < D * BM / 8; c += 256) {
-    const int d = c / (BM / 8), col = c % (BM / 8);
-    st_u32x4((bf16 *)a.qt + slab + d * BM + col * 8, ld_u32x4(&tq[d][col * 8]));
-    st_u32x4((bf16 *)a.dot + slab + d * BM + col * 8, ld_u32x4(&tdo[d][col * 8]));
-  }
+  for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, TPR);
+  if (valid && sub == 0) a.delta[(int64_t)h * a.n_q + r] = dot;
 }
 
 // D/4 lanes per (row, head); each lane merges 4 consecutive elements.
@@ -167,22 +111,10 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float *acc, bf16
 
 }  // namespace
 
-hipError_t launch_transpose(const void *x, int64_t n, int32_t h_kv, int32_t d, int64_t kpad, bool permute,
-                            void *out, hipStream_t s) {
-  if (kpad == 0) return hipSuccess;
-  dim3 grid((unsigned)(kpad / 64), (unsigned)h_kv);
-  if (d == 128)
-    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, (const bf16 *)x, n, h_kv, kpad,
-                       permute ? 1 : 0, (bf16 *)out);
-  else
-    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, (const bf16 *)x, n, h_kv, kpad,
-                       permute ? 1 : 0, (bf16 *)out);
-  return hipGetLastError();
-}
-
 hipError_t launch_prepare(const PrepArgs &a, int32_t d, hipStream_t s) {
-  if (a.n_bq == 0) return hipSuccess;
-  dim3 grid((unsigned)a.n_bq, (unsigned)a.h_q);
+  if (a.n_q == 0) return hipSuccess;
+  const int rows_per_block = 256 / (d / 8);
+  dim3 grid((unsigned)((a.n_q + rows_per_block - 1) / rows_per_block), (unsigned)a.h_q);
   if (d == 128) hipLaunchKernelGGL(prepare_kernel<128>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(prepare_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -2,44 +2,39 @@
 //
 // Core attention softmax(Q K^T) V ("Efficient Long-context Language Model
 // Training by Core Attention Disaggregation", English abstract) restricted to
-// the legal pairs of the BDLM mask, computed against one clean K/V range and,
+// the legal pairs of the BDLM mask, against one clean K/V range and,
 // optionally, the rank's local corrupted K/V ("rit.work explainer of CSBP",
 // section on why conventional context parallelism sends extra data).  Writes
 // the range's partial O and its log-sum-exp, so that partials over disjoint
 // ranges merge exactly.
 //
-// Layout of the work: one workgroup = 4 waves = 128 query rows of one q-head.
-// Each wave owns 32 rows and computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
-// so a lane holds one query (column) and 16 of its keys: the row max needs one
-// cross-half exchange and the row sum stays in-lane.  The probabilities are fed
-// straight from the C registers into O^T += V^T P^T as the B operand; V^T is
-// read from a transposed copy whose keys are pre-permuted to match.
-// Full key tiles skip the mask; partial tiles compare each key against the
-// row's legal range.  The running max is only raised (and O, l rescaled) when
-// it grows by more than 2^8, which keeps every probability below 256.
+// One workgroup = 4 waves = 128 query rows of one q-head; each wave owns 32
+// rows.  S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane and 16
+// of its keys in the lane's C registers: the row max needs one exchange across
+// the wave halves and the row sum stays in-lane.  The probabilities go straight
+// from the C registers into O^T += V^T P^T as the B operand; V^T comes from
+// transpose reads of the row-major V tile.  K and V stream through two LDS
+// buffers filled by direct global->LDS loads while the previous tile computes.
+// Full key tiles skip the mask; partial tiles compare each key with the row's
+// legal range.  The running max is only raised (rescaling O and l) when it grows
+// by more than 2^8, which keeps every probability below 256.
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 namespace bdattn {
 namespace {
 
 template <int D>
-struct __attribute__((aligned(16))) FwdSmem {
-  static constexpr int KS = D + 8;                 // K tile row stride (elements)
-  static constexpr int VS = BDATTN_FWD_BN + 8;     // V^T tile row stride
-  bf16 k[BDATTN_FWD_BN * KS];
-  bf16 vt[D * VS];
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int BN = BDATTN_FWD_BN;
-  constexpr int NC = D / 16;                 // 16-wide chunks of the head dim
-  constexpr int ND = D / 32;                 // 32-wide tiles of the head dim
-  constexpr int KCH = BN * D / 8 / 256;      // 16-byte chunks per thread, K tile
-  constexpr int VCH = D * BN / 8 / 256;      // 16-byte chunks per thread, V^T tile
-  using Sm = FwdSmem<D>;
-  __shared__ Sm sm;
+  static_assert(BN == Tile<D>::ROWS, "key tile = one LDS tile");
+  constexpr int NC = D / 16, ND = D / 32;
+  constexpr int VMN = 2 * Tile<D>::LOADS / BDATTN_FWD_WAVES;   // direct loads per thread per tile
+  __shared__ __attribute__((aligned(1024))) char ks0[Tile<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs0[Tile<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char ks1[Tile<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vs1[Tile<D>::BYTES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, g = lane >> 5;
   const int item = blockIdx.x / a.h_q;
@@ -55,88 +50,55 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     const int lmin = it[2 + 4 * s], lmax = it[3 + 4 * s], hmin = it[4 + 4 * s], hmax = it[5 + 4 * s];
     lo_max[s] = lmax;
     hi_min[s] = hmin;
-    if (hmax > lmin) {
-      base[s] = lmin / BN * BN;
-      nt[s] = (hmax - base[s] + BN - 1) / BN;
-    } else {
-      base[s] = 0;
-      nt[s] = 0;
-    }
+    base[s] = lmin / BN * BN;
+    nt[s] = hmax > lmin ? (hmax - base[s] + BN - 1) / BN : 0;
   }
   const int total = nt[0] + nt[1];
 
   const int rloc = wave * 32 + j;
   const bool valid = rloc < nrows;
-  const int row = q0 + rloc;
+  const int row = q0 + (valid ? rloc : 0);
 
-  // Q as the B operand of S^T = K Q^T: lane (query j, group g) holds d = 16c + 8g .. +7.
+  // Q as the B operand of S^T = K Q^T: lane (query j, half g) holds d = 16c + 8g .. +7.
   bf16x8 qf[NC];
   {
     const bf16 *qrow = (const bf16 *)a.q + ((int64_t)row * a.h_q + h) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = valid ? ld_bf16x8(qrow + 16 * c + 8 * g) : zero_bf16x8();
   }
-  int lo[2] = {0, 0}, hi[2] = {0, 0};
+  int lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
   if (valid) {
-    u32x4 rb = ld_u32x4(a.rows + (int64_t)row * 4);
-    lo[0] = (int)rb[0]; hi[0] = (int)rb[1]; lo[1] = (int)rb[2]; hi[1] = (int)rb[3];
+    const u32x4 rb = ld_u32x4(a.rows + (int64_t)row * 4);
+    lo0 = (int)rb[0]; hi0 = (int)rb[1]; lo1 = (int)rb[2]; hi1 = (int)rb[3];
   }
 
   f32x16 oacc[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) oacc[dt] = zero_f32x16();
-  float m_used = -INFINITY;   // running max in log2 units, same in both halves of a query
+  float m_used = -INFINITY;   // running max in log2 units, equal in both halves of a query
   double l_sum = 0.0;         // this lane's share of the row sum
 
-  u32x4 kreg[KCH], vreg[VCH];
-  auto tile_seg = [&](int t) { return t < nt[0] ? 0 : 1; };
-  auto tile_k0 = [&](int t) { return t < nt[0] ? base[0] + t * BN : base[1] + (t - nt[0]) * BN; };
-  auto load_tile = [&](int t) {
-    const int s = tile_seg(t), k0 = tile_k0(t);
-    const bf16 *kb = (const bf16 *)a.k[s];
-    const bf16 *vb = (const bf16 *)a.vt[s] + (int64_t)kvh * D * a.kpad[s] + k0;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, r = c / (D / 8), col = c % (D / 8), key = k0 + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = key < a.n_seg[s] ? ld_u32x4(kb + ((int64_t)key * a.h_kv + kvh) * D + col * 8) : z;
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i, r = c / (BN / 8), col = c % (BN / 8);
-      vreg[i] = ld_u32x4(vb + (int64_t)r * a.kpad[s] + col * 8);
-    }
+  const int64_t kv_stride = (int64_t)a.h_kv * D;
+  auto issue = [&](int t, char *kd, char *vd) {
+    const int s = t < nt[0] ? 0 : 1;
+    const int k0 = s == 0 ? base[0] + t * BN : base[1] + (t - nt[0]) * BN;
+    const int64_t off = (int64_t)k0 * kv_stride + kvh * D;
+    const int nv = a.n_seg[s] - k0;
+    tile_load<D, BDATTN_FWD_WAVES>(kd, (const bf16 *)a.k[s] + off, kv_stride, nv, wave, lane);
+    tile_load<D, BDATTN_FWD_WAVES>(vd, (const bf16 *)a.v[s] + off, kv_stride, nv, wave, lane);
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, r = c / (D / 8), col = c % (D / 8);
-      st_u32x4(&sm.k[r * Sm::KS + col * 8], kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i, r = c / (BN / 8), col = c % (BN / 8);
-      st_u32x4(&sm.vt[r * Sm::VS + col * 8], vreg[i]);
-    }
-  };
-
-  if (total > 0) load_tile(0);
-  for (int t = 0; t < total; ++t) {
-    const int s = tile_seg(t), k0 = tile_k0(t);
+  auto compute = [&](int t, const char *kt_lds, const char *vt_lds) {
+    const int s = t < nt[0] ? 0 : 1;
+    const int k0 = s == 0 ? base[0] + t * BN : base[1] + (t - nt[0]) * BN;
     const bool full = lo_max[s] <= k0 && k0 + BN <= hi_min[s];
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < total) load_tile(t + 1);
-
-    // S^T for two 32-key tiles: lane holds keys 8(r/4) + 4g + r%4 of query j.
+    const int lo = s ? lo1 : lo0, hi = s ? hi1 : hi0;
     f32x16 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sc[kt] = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sc[kt] = mfma32(ld_bf16x8(&sm.k[(kt * 32 + j) * Sm::KS + 16 * c + 8 * g]), qf[c], sc[kt]);
+        sc[kt] = mfma32(tile_row8<D>(kt_lds, kt * 32 + j, 16 * c + 8 * g), qf[c], sc[kt]);
     }
     if (!full) {
 #pragma unroll
@@ -144,7 +106,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key < lo[s] || key >= hi[s]) sc[kt][r] = -INFINITY;
+          if (key < lo || key >= hi) sc[kt][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -175,14 +137,37 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         psum += pv;
       }
     l_sum += (double)psum;
-
-    // O^T += V^T P^T over four 16-key chunks.
 #pragma unroll
-    for (int c16 = 0; c16 < 4; ++c16) {
+    for (int c16 = 0; c16 < BN / 16; ++c16) {
       const bf16x8 pb = pack8(sc[c16 >> 1], 8 * (c16 & 1));
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
-        oacc[dt] = mfma32(ld_bf16x8(&sm.vt[(32 * dt + j) * Sm::VS + 16 * c16 + 8 * g]), pb, oacc[dt]);
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma32(tile_tr8<D>(vt_lds, c16, dt, lane), pb, oacc[dt]);
+    }
+  };
+
+  if (total > 0) issue(0, ks0, vs0);
+  for (int t = 0; t < total; t += 2) {
+    if (t + 1 < total) {
+      issue(t + 1, ks1, vs1);
+      wait_vmcnt<VMN>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wg_barrier();
+    compute(t, ks0, vs0);
+    wait_lgkm0();
+    wg_barrier();
+    if (t + 1 < total) {
+      if (t + 2 < total) {
+        issue(t + 2, ks0, vs0);
+        wait_vmcnt<VMN>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      wg_barrier();
+      compute(t + 1, ks1, vs1);
+      wait_lgkm0();
+      wg_barrier();
     }
   }
 

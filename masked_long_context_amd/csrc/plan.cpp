@@ -150,19 +150,7 @@ void finish(Plan &p) {
   if (!p.kt.empty()) std::memcpy(p.image.data() + h.off_kt, p.kt.data(), p.kt.size() * sizeof(KTile));
   if (!p.list.empty()) std::memcpy(p.image.data() + h.off_list, p.list.data(), p.list.size() * 4);
 
-  // Workspace: image | transposed K or V of segment 0 | of segment 1.
-  off = h.image_bytes;
-  for (int s = 0; s < 2; ++s) {
-    p.kpad[s] = align_up(p.n_seg[s], BDATTN_KPAD);
-    p.ws_t_off[s] = off;
-    off = align_up(off + (int64_t)p.h_kv * p.d * p.kpad[s] * 2, BDATTN_ALIGN);
-  }
-  p.ws_bytes = off;
-  // Prepare buffer: per backward q-tile, transposed Q and dO slabs [h_q][d][BM].
-  int64_t slab = (int64_t)p.bq.size() * p.h_q * p.d * BDATTN_BWD_BM * 2;
-  p.prep_q_off = 0;
-  p.prep_do_off = align_up(slab, BDATTN_ALIGN);
-  p.prep_bytes = p.prep_do_off + align_up(slab, BDATTN_ALIGN);
+  p.ws_bytes = h.image_bytes;
   p.id = g_next_id.fetch_add(1);
 }
 

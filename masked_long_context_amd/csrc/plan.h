@@ -40,10 +40,8 @@ struct Plan {
   // Device image of the tables (uploaded into the head of each workspace).
   std::vector<uint8_t> image;
   ImageHeader hdr{};
-  // Workspace and prepare-buffer layout.
-  int64_t ws_t_off[2] = {0, 0}, ws_bytes = 0;
-  int64_t kpad[2] = {0, 0};
-  int64_t prep_q_off = 0, prep_do_off = 0, prep_bytes = 0;
+  // Workspace = the uploaded tables.
+  int64_t ws_bytes = 0;
   // Pinned copy of `image` for asynchronous uploads (made on first use).
   void *pinned = nullptr;
   bool used = false;

@@ -7,7 +7,7 @@ Training", English abstract).  The step runs, on one HIP stream:
 
     for each clean K/V shard s:  bdattn_fwd  -> partial (O_s, LSE_s)
     bdattn_lse_merge             -> O, LSE
-    bdattn_bwd_prepare           -> delta, transposed Q/dO tiles
+    bdattn_bwd_prepare           -> delta, cleared dQ accumulator
     for each clean K/V shard s:  bdattn_bwd  -> dQ (accumulated), dK_s, dV_s
     bdattn_dq_finalize           -> dQ (bf16)
 
@@ -37,7 +37,6 @@ class BdlmRankStep:
         p = problem
         self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
         self.ws = B.workspace(max(pl.workspace_bytes for pl in self.plans), device)
-        self.prep = B.workspace(max(pl.prepare_bytes for pl in self.plans), device)
         n_parts = max(1, len(self.active))
         self.o_parts = torch.empty((n_parts, self.n_q, self.h_q, self.d), dtype=part_dtype, device=device)
         self.lse_parts = torch.empty((n_parts, self.h_q, self.n_q), dtype=torch.float32, device=device)
@@ -80,12 +79,12 @@ class BdlmRankStep:
 
     def backward(self, q, k_clean, v_clean, k_corr, v_corr, dout):
         with self._t("prepare"):
-            B.bdattn_bwd_prepare(self.plans[0], q, self.o, dout, self.delta, self.dq_acc, self.prep)
+            B.bdattn_bwd_prepare(self.plans[0], self.o, dout, self.delta, self.dq_acc)
         for i, (off, n, local) in enumerate(self.shards):
             with self._t("bwd"):
                 B.bdattn_bwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
                              k_corr if local else None, v_corr if local else None, dout, self.lse,
-                             self.delta, self.prep, self.dq_acc, self.dk_clean[off:off + n],
+                             self.delta, self.dq_acc, self.dk_clean[off:off + n],
                              self.dv_clean[off:off + n], self.dk_corr if local else None,
                              self.dv_corr if local else None, self.ws)
         with self._t("finalize"):
@@ -105,7 +104,6 @@ class VarlenStep:
         T = int(cu_seqlens[-1])
         self.T, self.h_q, self.h_kv, self.d = T, h_q, h_kv, head_dim
         self.ws = B.workspace(self.plan.workspace_bytes, device)
-        self.prep = B.workspace(self.plan.prepare_bytes, device)
         self.o = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((h_q, T), dtype=torch.float32, device=device)
         self.delta = torch.empty((h_q, T), dtype=torch.float32, device=device)
@@ -123,8 +121,8 @@ class VarlenStep:
         return self.o, self.lse
 
     def backward(self, q, k, v, dout):
-        B.bdattn_bwd_prepare(self.plan, q, self.o, dout, self.delta, self.dq_acc, self.prep)
-        B.bdattn_varlen_bwd(self.plan, q, k, v, dout, self.lse, self.delta, self.prep, self.dq_acc,
+        B.bdattn_bwd_prepare(self.plan, self.o, dout, self.delta, self.dq_acc)
+        B.bdattn_varlen_bwd(self.plan, q, k, v, dout, self.lse, self.delta, self.dq_acc,
                             self.dk, self.dv, self.ws)
         B.bdattn_dq_finalize(self.dq_acc, self.dq)
         return self.dq, self.dk, self.dv

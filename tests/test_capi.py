@@ -117,16 +117,20 @@ def test_bwd_and_prepare_argument_errors():
     plan = B.Plan.bdlm(**_problem())
     good = FakeTensor(1 << 20)
     f32 = FakeTensor(1 << 20, dtype=torch.float32)
-    prep_small = FakeTensor(1 << 20, numel=64)
     st = FakeStream()
     args = dict(q=good, k_clean=good, v_clean=good, k_corr=good, v_corr=good, dout=good, lse=f32,
-                delta=f32, prep=good, dq_accum=f32, dk_clean=good, dv_clean=good, dk_corr=good,
+                delta=f32, dq_accum=f32, dk_clean=good, dv_clean=good, dk_corr=good,
                 dv_corr=good, ws=good, stream=st)
     assert _status(lambda: B.bdattn_bwd(plan, **{**args, "dk_clean": None})) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "prep": prep_small})) == B.EWORKSPACE
-    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "prep": FakeTensor((1 << 20) + 64)})) == B.EALIGN
-    assert _status(lambda: B.bdattn_bwd_prepare(plan, good, good, good, f32, f32, prep_small, st)) == B.EWORKSPACE
-    assert _status(lambda: B.bdattn_bwd_prepare(plan, good, None, good, f32, f32, good, st)) == B.EINVAL
+    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "dv_corr": None})) == B.EINVAL
+    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "ws": FakeTensor(1 << 20, numel=8)})) == B.EWORKSPACE
+    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "lse": FakeTensor((1 << 20) + 4)})) == B.EALIGN
+    assert _status(lambda: B.bdattn_bwd_prepare(plan, None, good, f32, f32, st)) == B.EINVAL
+    assert _status(lambda: B.bdattn_bwd_prepare(plan, good, good, None, None, st)) == B.EINVAL
+    assert _status(lambda: B.bdattn_bwd_prepare(plan, FakeTensor(1 << 20, dtype=torch.float16), good, f32,
+                                                None, st)) == B.EUNSUPPORTED
+    vplan = B.Plan.varlen([0, 100], True, 4, 2, 128)
+    assert _status(lambda: B.bdattn_bwd(vplan, **args)) == B.EINVAL
 
 
 def test_merge_and_finalize_argument_errors():
@@ -150,7 +154,6 @@ def test_plan_sizes_and_counts():
     assert plan.n_q == 64 + 2 * 32
     assert plan.n_kv(0) == 128 and plan.n_kv(1) == 64
     assert plan.workspace_bytes > 0 and plan.workspace_bytes % 256 == 0
-    assert plan.prepare_bytes > 0
     # clean rows at positions 64..127 (blocks 2, 3) see keys [0, 96) and [0, 128) of the range;
     # block 3 sees [0, 96) plus its own 32; block 1 sees [0, 32) plus its own 32
     assert plan.useful_pairs == 32 * 96 + 32 * 128 + 32 * (96 + 32) + 32 * (32 + 32)

@@ -126,16 +126,15 @@ def test_rows_without_keys_and_empty_ranges():
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
     # backward of the empty range: gradients of its keys are exactly zero, dQ untouched
-    prep = B.workspace(plan.prepare_bytes)
     delta = torch.zeros((2, p.n_q), device="cuda")
     dq = torch.zeros((p.n_q, 2, 128), device="cuda")
     ob = torch.zeros((p.n_q, 2, 128), dtype=torch.bfloat16, device="cuda")
     do = inp["dout"].cuda()
-    B.bdattn_bwd_prepare(plan, q, ob, do, delta, None, prep)
+    B.bdattn_bwd_prepare(plan, ob, do, delta, None)
     dk = torch.full((256, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     dv = torch.full_like(dk, float("nan"))
     full_lse = torch.zeros((2, p.n_q), device="cuda")
-    B.bdattn_bwd(plan, q, kc, vc, None, None, do, full_lse, delta, prep, dq, dk, dv, None, None, ws)
+    B.bdattn_bwd(plan, q, kc, vc, None, None, do, full_lse, delta, dq, dk, dv, None, None, ws)
     torch.cuda.synchronize()
     assert torch.all(dk == 0) and torch.all(dv == 0) and torch.all(dq == 0)
 
