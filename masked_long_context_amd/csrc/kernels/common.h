@@ -64,4 +64,12 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &c, int r0) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Read of a table that no kernel writes while it runs, through the constant
+// address space: with a uniform address this becomes a scalar (SMEM) load,
+// which waits on lgkmcnt and so never stalls behind in-flight vector loads.
+template <class T>
+__device__ __forceinline__ T ld_table(const T *p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
 }  // namespace bdattn

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char ks1[Tile<D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vs1[Tile<D>::BYTES];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, j = lane & 31, g = lane >> 5;
   const int item = blockIdx.x / a.h_q;
   const int pslot = blockIdx.x % a.h_q;
   // consecutive workgroups land on different XCDs: give each XCD one KV head
@@ -72,13 +72,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     lo0 = (int)rb[0]; hi0 = (int)rb[1]; lo1 = (int)rb[2]; hi1 = (int)rb[3];
   }
 
+  const RowReader<D> rd(lane);
+  const TrReader<D> tr(lane);
   f32x16 oacc[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) oacc[dt] = zero_f32x16();
   float m_used = -INFINITY;   // running max in log2 units, equal in both halves of a query
   double l_sum = 0.0;         // this lane's share of the row sum
 
-  const int64_t kv_stride = (int64_t)a.h_kv * D;
+  const int kv_stride = a.h_kv * D;
   auto issue = [&](int t, char *kd, char *vd) {
     const int s = t < nt[0] ? 0 : 1;
     const int k0 = s == 0 ? base[0] + t * BN : base[1] + (t - nt[0]) * BN;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       sc[kt] = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sc[kt] = mfma32(tile_row8<D>(kt_lds, kt * 32 + j, 16 * c + 8 * g), qf[c], sc[kt]);
+        sc[kt] = mfma32(rd(kt_lds, kt, c), qf[c], sc[kt]);
     }
     if (!full) {
 #pragma unroll
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int c16 = 0; c16 < BN / 16; ++c16) {
       const bf16x8 pb = pack8(sc[c16 >> 1], 8 * (c16 & 1));
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma32(tile_tr8<D>(vt_lds, c16, dt, lane), pb, oacc[dt]);
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma32(tr(vt_lds, c16, dt), pb, oacc[dt]);
     }
   };
 

@@ -41,23 +41,28 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
   return row * (2 * D) + ((chunk ^ tile_swz(row)) << 4);
 }
 
-// This wave's share of the asynchronous copy of 64 rows starting at `g` (row
-// stride `stride` elements).  Rows at or beyond `nvalid` re-read row nvalid - 1
-// (the caller masks them); nvalid >= 1.  Issues Tile<D>::LOADS / NW loads.
+// This wave's share of the asynchronous copy of 64 rows starting at `g` (a
+// wave-uniform pointer; row stride `stride` elements, 64 * stride < 2^30).  Rows
+// at or beyond `nvalid` re-read row nvalid - 1 (the caller masks them);
+// nvalid >= 1.  `wave` must be wave-uniform.  Issues Tile<D>::LOADS / NW loads.
 template <int D, int NW>
-__device__ __forceinline__ void tile_load(char *lds, const bf16 *g, int64_t stride, int nvalid, int wave,
-                                          int lane) {
+__device__ __forceinline__ void tile_load(char *lds, const bf16 *g, int stride, int nvalid, int wave, int lane) {
   constexpr int PER = Tile<D>::LOADS / NW;
   static_assert(Tile<D>::LOADS % NW == 0, "tile loads must split evenly over the waves");
+  const char *gb = reinterpret_cast<const char *>(g);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int kb = wave * PER + i;
     const int row = kb * Tile<D>::RPK + lane / Tile<D>::CPR;
     const int c = (lane % Tile<D>::CPR) ^ tile_swz(row);
     const int rr = row < nvalid ? row : nvalid - 1;
-    __builtin_amdgcn_global_load_lds(g + (int64_t)rr * stride + c * 8, BD_LDS(lds + kb * 1024), 16, 0, 0);
+    const uint32_t off = (uint32_t)(rr * stride + c * 8) * 2u;
+    __builtin_amdgcn_global_load_lds(gb + off, BD_LDS(lds + kb * 1024), 16, 0, 0);
   }
 }
+
+// Wave index as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // 8 consecutive elements [col, col + 8) of one row (col a multiple of 8).
 template <int D>
@@ -81,6 +86,51 @@ __device__ __forceinline__ bf16x8 tile_tr8(const char *t, int c16, int mt, int l
   const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
+
+// Row reads of a tile with a fixed lane pattern: row 32 t + (lane % 32), columns
+// 16 c + 8 (lane / 32) .. +7 (the A/B operand of a 32x32x16 MFMA over the head
+// dim).  For this lane, swz(row) = s is constant, and the physical chunk is
+// (2c + g) ^ s = 2 (c ^ (s >> 1)) + (g ^ (s & 1)); with c = 4m + n only n sees
+// the XOR, so four per-lane offsets (n = 0..3) plus immediates cover every read.
+template <int D>
+struct RowReader {
+  int off[4];
+  __device__ __forceinline__ explicit RowReader(int lane) {
+    const int j = lane & 31, g = lane >> 5, sw = tile_swz(j);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) off[n] = j * (2 * D) + 32 * (n ^ (sw >> 1)) + 16 * (g ^ (sw & 1));
+  }
+  __device__ __forceinline__ bf16x8 operator()(const char *t, int tb, int c) const {
+    return *reinterpret_cast<const bf16x8 *>(t + off[c & 3] + 128 * (c >> 2) + tb * 32 * (2 * D));
+  }
+};
+
+// Transpose reads (tile_tr8) with a fixed lane pattern.  Row bits 0..2 depend on
+// the lane only, so s = swz(row) is constant; the chunk (4 mt + r) ^ s =
+// 4 (mt ^ (s >> 2)) + (r ^ (s & 3)), and with mt = 2m + n only n sees the XOR:
+// two per-lane offsets (n = 0, 1) plus immediates.
+template <int D>
+struct TrReader {
+  int off[2];
+  __device__ __forceinline__ explicit TrReader(int lane) {
+    const int i = lane & 15, G = lane >> 4;
+    const int rl = 4 * (G >> 1) + (i >> 2);              // row within a 16-row chunk, bits 0..2
+    const int sw = tile_swz(rl);
+    const int r = 2 * (G & 1) + ((i >> 1) & 1);          // chunk within a 32-column tile
+    const int sub = 8 * (i & 1);                         // byte offset inside the chunk
+#pragma unroll
+    for (int n = 0; n < 2; ++n) off[n] = rl * (2 * D) + 64 * (n ^ (sw >> 2)) + 16 * (r ^ (sw & 3)) + sub;
+  }
+  // Same operand as tile_tr8<D>(t, c16, mt, lane).
+  __device__ __forceinline__ bf16x8 operator()(const char *t, int c16, int mt) const {
+    const char *p = t + off[mt & 1] + 128 * (mt >> 1) + 16 * c16 * (2 * D);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(BD_LDS_V4I16(p));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(BD_LDS_V4I16(p + 8 * (2 * D)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+  }
+};
 
 // s_waitcnt with vmcnt(N) and the other counters left free (gfx9 encoding).
 template <int N>
