@@ -99,7 +99,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=32)
+    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} refused: this BDLM attention path runs on one GPU "
@@ -139,17 +141,29 @@ def main():
     tot = timer.totals_ms()
     tflops = flops / (ms * 1e-3) / 1e12
 
-    # dominant kernel: the backward (10d of the 14d flops per pair)
-    bwd_ms, bwd_n = tot.get("bwd", (0.0, 1))
-    bwd_flops_per_launch = pairs * p.h_q * 10 * p.head_dim / len(cfg.shards)
-    bwd_avg_ms = bwd_ms / bwd_n
-    bwd_achieved = bwd_flops_per_launch / (bwd_avg_ms * 1e-3) / 1e12
-    fwd_ms, fwd_n = tot.get("fwd", (0.0, 1))
-    fwd_achieved = pairs * p.h_q * 4 * p.head_dim * args.steps / (fwd_ms * 1e-3) / 1e12 if fwd_ms else 0.0
+    # per-kernel rates from the events around each library call (one kernel per call)
+    n_sh = len(cfg.shards)
     n_act = len(step.active)
+    per = {}
+    for tag, dflops in (("fwd", 4), ("dkdv", 8), ("dq", 6)):
+        tms, tn = tot.get(tag, (0.0, 1))
+        per[tag] = dict(ms_per_step=tms / args.steps, launches_per_step=tn // args.steps,
+                        ms_per_launch=tms / tn,
+                        tflops=pairs * p.h_q * dflops * p.head_dim * args.steps / (tms * 1e-3) / 1e12 if tms else 0.0)
+    # dominant kernel: the key-major dK/dV kernel (8d flops per useful pair and q-head)
+    dk = per["dkdv"]
+    dk_flops_per_launch = pairs * p.h_q * 8 * p.head_dim / n_sh
+    dk_achieved = dk_flops_per_launch / (dk["ms_per_launch"] * 1e-3) / 1e12
     merge_ms, merge_n = tot.get("merge", (0.0, 1))
     merge_bytes = p.n_q * p.h_q * (n_act * (4 * p.head_dim + 4) + (2 * p.head_dim + 4))
     merge_gbs = merge_bytes / (merge_ms / merge_n * 1e-3) / 1e9 if merge_ms else 0.0
+    if args.copy_calibration:
+        # a plain copy of known size, for scaling HBM counters read by rocprofv3
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# bench: copy calibration moved {src.numel() * 4} bytes each way", file=sys.stderr, flush=True)
 
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -160,14 +174,12 @@ def main():
                    "clean_shards": len(cfg.shards), "useful_pairs_per_head": pairs,
                    "flops_per_step": flops},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "bwd_kernel<128>", "bound": "mfma", "achieved": round(bwd_achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+        "roofline": {"kernel": f"dkdv_kernel<{p.head_dim}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "ms_per_launch": round(dk["ms_per_launch"], 4),
+                     "flops_per_launch": dk_flops_per_launch},
         "kernels": {
-            "bwd": {"ms_per_launch": round(bwd_avg_ms, 4), "launches_per_step": len(cfg.shards),
-                    "tflops": round(bwd_achieved, 2)},
-            "fwd": {"ms_per_step": round(fwd_ms / args.steps, 3), "launches_per_step": n_act,
-                    "tflops": round(fwd_achieved, 2)},
+            **{k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
             "merge": {"ms": round(merge_ms / max(merge_n, 1), 4), "parts": n_act, "gbs": round(merge_gbs, 1),
                       "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4)},
             "prepare_ms": round(tot.get("prepare", (0.0, 1))[0] / args.steps, 4),

@@ -170,6 +170,21 @@ int bdattn_bwd(const bdattn_plan *plan, const void *q, const void *k_clean, cons
                const float *delta, float *dq_accum, void *dk_clean, void *dv_clean, void *dk_corr,
                void *dv_corr, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* The two steps of bdattn_bwd as separate calls (same kernels, same launch
+ * configuration), for callers that schedule or time them apart:
+ * bdattn_bwd_dkdv writes dK/dV of the range (key-major kernel);
+ * bdattn_bwd_dq adds the range's contribution to dq_accum (query-major kernel).
+ * Either works on a BDLM or a varlen plan (varlen: pass the packed K/V as the
+ * clean range and NULL for the corrupted pointers). */
+int bdattn_bwd_dkdv(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
+                    const void *k_corr, const void *v_corr, const void *dout, const float *lse,
+                    const float *delta, void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+int bdattn_bwd_dq(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
+                  const void *k_corr, const void *v_corr, const void *dout, const float *lse,
+                  const float *delta, float *dq_accum, void *workspace, int64_t workspace_bytes,
+                  void *stream);
+
 /* dq (bf16) = dq_accum (fp32), n_elems elements. */
 int bdattn_dq_finalize(const float *dq_accum, void *dq, int64_t n_elems, void *stream);
 

@@ -54,6 +54,8 @@ _SIGS = {
                                    c_int32, c_void_p, c_void_p]),
     "bdattn_bwd_prepare": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bdattn_bwd": (c_int32, [c_void_p] * 15 + [c_int64, c_void_p]),
+    "bdattn_bwd_dkdv": (c_int32, [c_void_p] * 14 + [c_int64, c_void_p]),
+    "bdattn_bwd_dq": (c_int32, [c_void_p] * 11 + [c_int64, c_void_p]),
     "bdattn_dq_finalize": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_fwd": (c_int32, [c_void_p] * 5 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_bwd": (c_int32, [c_void_p] * 11 + [c_int64, c_void_p]),
@@ -212,6 +214,19 @@ def bdattn_bwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta
     _check(lib().bdattn_bwd(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
                             _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(dk_clean), _ptr(dv_clean),
                             _ptr(dk_corr), _ptr(dv_corr), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def bdattn_bwd_dkdv(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta,
+                    dk_clean, dv_clean, dk_corr, dv_corr, ws, stream=None):
+    _check(lib().bdattn_bwd_dkdv(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
+                                 _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk_clean), _ptr(dv_clean), _ptr(dk_corr),
+                                 _ptr(dv_corr), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def bdattn_bwd_dq(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq_accum, ws, stream=None):
+    _check(lib().bdattn_bwd_dq(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
+                               _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(ws), ws.numel(),
+                               _stream(stream)))
 
 
 def bdattn_varlen_bwd(plan: Plan, q, k, v, dout, lse, delta, dq_accum, dk, dv, ws, stream=None):

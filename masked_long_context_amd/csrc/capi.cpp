@@ -136,7 +136,8 @@ int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
 
 int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
             const void *v1, const void *dout, const float *lse, const float *delta, float *dq, void *dk0,
-            void *dv0, void *dk1, void *dv1, void *ws, int64_t ws_bytes, void *stream) {
+            void *dv0, void *dk1, void *dv1, void *ws, int64_t ws_bytes, void *stream, bool do_dkdv = true,
+            bool do_dq = true) {
   bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
   const bdattn::Plan &p = pl->p;
   const bool rows = p.n_q > 0;
@@ -146,15 +147,15 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   CHECK_PTR(dout, work);
   CHECK_PTR(lse, work);
   CHECK_PTR(delta, work);
-  CHECK_PTR(dq, work);
+  CHECK_PTR(dq, work && do_dq);
   CHECK_PTR(k0, p.n_seg[0] > 0);
   CHECK_PTR(v0, p.n_seg[0] > 0);
-  CHECK_PTR(dk0, p.n_seg[0] > 0);
-  CHECK_PTR(dv0, p.n_seg[0] > 0);
+  CHECK_PTR(dk0, p.n_seg[0] > 0 && do_dkdv);
+  CHECK_PTR(dv0, p.n_seg[0] > 0 && do_dkdv);
   CHECK_PTR(k1, p.n_seg[1] > 0);
   CHECK_PTR(v1, p.n_seg[1] > 0);
-  CHECK_PTR(dk1, p.n_seg[1] > 0);
-  CHECK_PTR(dv1, p.n_seg[1] > 0);
+  CHECK_PTR(dk1, p.n_seg[1] > 0 && do_dkdv);
+  CHECK_PTR(dv1, p.n_seg[1] > 0 && do_dkdv);
   int rc = check_ws(p, ws, ws_bytes);
   if (rc != BDATTN_OK) return rc;
   if (!any_keys) return BDATTN_OK;
@@ -191,7 +192,7 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   a.group = p.h_q / p.h_kv;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
-  HIP_CHECK(bdattn::launch_bwd(a, p.d, s), "backward kernels");
+  HIP_CHECK(bdattn::launch_bwd(a, p.d, s, do_dkdv, do_dq), "backward kernels");
   return BDATTN_OK;
 }
 
@@ -297,6 +298,23 @@ int bdattn_bwd(const bdattn_plan *pl, const void *q, const void *k_clean, const 
   if (pl->p.kind != 0) return fail(BDATTN_EINVAL, "plan is a varlen plan; use bdattn_varlen_bwd");
   return run_bwd(pl, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq, dk_clean, dv_clean, dk_corr,
                  dv_corr, ws, ws_bytes, stream);
+}
+
+int bdattn_bwd_dkdv(const bdattn_plan *pl, const void *q, const void *k_clean, const void *v_clean,
+                    const void *k_corr, const void *v_corr, const void *dout, const float *lse, const float *delta,
+                    void *dk_clean, void *dv_clean, void *dk_corr, void *dv_corr, void *ws, int64_t ws_bytes,
+                    void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  return run_bwd(pl, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, nullptr, dk_clean, dv_clean, dk_corr,
+                 dv_corr, ws, ws_bytes, stream, true, false);
+}
+
+int bdattn_bwd_dq(const bdattn_plan *pl, const void *q, const void *k_clean, const void *v_clean,
+                  const void *k_corr, const void *v_corr, const void *dout, const float *lse, const float *delta,
+                  float *dq_accum, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  return run_bwd(pl, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq_accum, nullptr, nullptr, nullptr,
+                 nullptr, ws, ws_bytes, stream, false, true);
 }
 
 int bdattn_varlen_bwd(const bdattn_plan *pl, const void *q, const void *k, const void *v, const void *dout,

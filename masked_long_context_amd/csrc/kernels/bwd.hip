@@ -392,15 +392,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s) {
-  const int64_t kblocks = (int64_t)a.n_kt * a.h_kv;
+hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, bool dq) {
+  const int64_t kblocks = dkdv ? (int64_t)a.n_kt * a.h_kv : 0;
   if (kblocks > 0) {
     if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)kblocks), dim3(512), 0, s, a);
     else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)kblocks), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t qblocks = (int64_t)a.n_items * a.h_q;
+  const int64_t qblocks = dq ? (int64_t)a.n_items * a.h_q : 0;
   if (qblocks > 0) {
     if (d == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)qblocks), dim3(256), 0, s, a);

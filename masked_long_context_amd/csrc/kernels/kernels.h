@@ -43,7 +43,7 @@ struct PrepArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a, int32_t d, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, bool dq);
 hipError_t launch_prepare(const PrepArgs &a, int32_t d, hipStream_t s);
 hipError_t launch_merge(int32_t n_parts, const void *o_parts, bool parts_f32, const float *lse_parts,
                         int64_t n_rows, int32_t h, int32_t d, void *o_out, bool out_f32, float *lse_out,

@@ -8,7 +8,7 @@ Training", English abstract).  The step runs, on one HIP stream:
     for each clean K/V shard s:  bdattn_fwd  -> partial (O_s, LSE_s)
     bdattn_lse_merge             -> O, LSE
     bdattn_bwd_prepare           -> delta, cleared dQ accumulator
-    for each clean K/V shard s:  bdattn_bwd  -> dQ (accumulated), dK_s, dV_s
+    for each clean K/V shard s:  bdattn_bwd_dkdv -> dK_s, dV_s; bdattn_bwd_dq -> dQ (accumulated)
     bdattn_dq_finalize           -> dQ (bf16)
 
 The local corrupted K/V join the call of one chosen shard.  Shards whose plan
@@ -80,13 +80,17 @@ class BdlmRankStep:
     def backward(self, q, k_clean, v_clean, k_corr, v_corr, dout):
         with self._t("prepare"):
             B.bdattn_bwd_prepare(self.plans[0], self.o, dout, self.delta, self.dq_acc)
+        # the two steps of bdattn_bwd, called apart so that each can be timed
         for i, (off, n, local) in enumerate(self.shards):
-            with self._t("bwd"):
-                B.bdattn_bwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
-                             k_corr if local else None, v_corr if local else None, dout, self.lse,
-                             self.delta, self.dq_acc, self.dk_clean[off:off + n],
-                             self.dv_clean[off:off + n], self.dk_corr if local else None,
-                             self.dv_corr if local else None, self.ws)
+            kc, vc = k_clean[off:off + n], v_clean[off:off + n]
+            kx, vx = (k_corr, v_corr) if local else (None, None)
+            with self._t("dkdv"):
+                B.bdattn_bwd_dkdv(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta,
+                                  self.dk_clean[off:off + n], self.dv_clean[off:off + n],
+                                  self.dk_corr if local else None, self.dv_corr if local else None, self.ws)
+            with self._t("dq"):
+                B.bdattn_bwd_dq(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta, self.dq_acc,
+                                self.ws)
         with self._t("finalize"):
             B.bdattn_dq_finalize(self.dq_acc, self.dq)
         return self.dq, self.dk_clean, self.dv_clean, self.dk_corr, self.dv_corr

@@ -131,6 +131,12 @@ def test_bwd_and_prepare_argument_errors():
                                                 None, st)) == B.EUNSUPPORTED
     vplan = B.Plan.varlen([0, 100], True, 4, 2, 128)
     assert _status(lambda: B.bdattn_bwd(vplan, **args)) == B.EINVAL
+    dk_args = {k: v for k, v in args.items() if k != "dq_accum"}
+    assert _status(lambda: B.bdattn_bwd_dkdv(plan, **{**dk_args, "dk_corr": None})) == B.EINVAL
+    assert _status(lambda: B.bdattn_bwd_dkdv(plan, **{**dk_args, "ws": FakeTensor(1 << 20, numel=8)})) == B.EWORKSPACE
+    dq_args = {k: v for k, v in args.items() if k not in ("dk_clean", "dv_clean", "dk_corr", "dv_corr")}
+    assert _status(lambda: B.bdattn_bwd_dq(plan, **{**dq_args, "dq_accum": None})) == B.EINVAL
+    assert _status(lambda: B.bdattn_bwd_dq(plan, **{**dq_args, "delta": FakeTensor((1 << 20) + 4)})) == B.EALIGN
 
 
 def test_merge_and_finalize_argument_errors():
