@@ -331,15 +331,23 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
         dp[kt] = mfma32(rd(v_lds, kt, c), df[c], dp[kt]);
       }
     }
+    if (!full) {
+      keep_branch();
+      // illegal pairs get S = -inf, hence P = 0
+      const int lo_r = lo - k0 - 4 * g, hi_r = hi - k0 - 4 * g;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = kt * 32 + 8 * (r >> 2) + (r & 3);
+          if (o < lo_r || o >= hi_r) sc[kt][r] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(sc[kt][r], a.scale_log2, -l2));
-        if (!full) {
-          const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key < lo || key >= hi) pv = 0.f;
-        }
+        const float pv = fast_exp2(fmaf(sc[kt][r], a.scale_log2, -l2));
         sc[kt][r] = pv * (dp[kt][r] - dl);     // dS^T
       }
 #pragma unroll

@@ -67,6 +67,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Read of a table that no kernel writes while it runs, through the constant
 // address space: with a uniform address this becomes a scalar (SMEM) load,
 // which waits on lgkmcnt and so never stalls behind in-flight vector loads.
+// Marks a branch the compiler must keep: code that contains it is never
+// speculated into straight-line selects.  Used on the rare partial-tile masks,
+// which would otherwise run on every tile.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::); }
+
 template <class T>
 __device__ __forceinline__ T ld_table(const T *p, int64_t i) {
   return ((const __attribute__((address_space(4))) T *)p)[i];

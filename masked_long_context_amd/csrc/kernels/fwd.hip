@@ -103,12 +103,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         sc[kt] = mfma32(rd(kt_lds, kt, c), qf[c], sc[kt]);
     }
     if (!full) {
+      keep_branch();
+      // key k0 + 4 g + o (o an immediate) is legal iff lo <= key < hi
+      const int lo_r = lo - k0 - 4 * g, hi_r = hi - k0 - 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key < lo || key >= hi) sc[kt][r] = -INFINITY;
+          const int o = kt * 32 + 8 * (r >> 2) + (r & 3);
+          if (o < lo_r || o >= hi_r) sc[kt][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
