@@ -29,6 +29,7 @@
 // The split recomputes S and dP once more than a fused kernel, but removes the
 // fp32 atomics a fused key-major kernel needs for dQ (about one per useful pair
 // and head), which the L2 executes far slower than the MFMA work they replace.
+#include <cfloat>
 #include <type_traits>
 
 #include "common.h"
@@ -38,25 +39,34 @@
 namespace bdattn {
 namespace {
 
-// The loop of one dkdv role.  Both roles walk the same (query tile, head)
-// sequence over the shared double-buffered Q/dO tiles and pass the same
-// barriers; per tile:
-//   phase A  role 0 (dV waves, hold K): S = Q K^T, P = exp(S - LSE) on the legal
-//            pairs; P (fp32) goes to LDS in the C-register layout.
-//            role 1 (dK waves, hold V): dP = dO V^T.
-//   barrier
-//   phase B  role 0: dV^T += dO^T P.
-//            role 1: reads P back (same lane <-> key map), dS = P o (dP - delta),
-//            dK^T += Q^T dS.
+// Static LDS of the dK/dV kernel.  Query tiles (Q) pass through three buffers and
+// dO tiles through two, because the dV waves run one tile ahead of the dK waves:
+// in iteration i they read Q(i + 1) and dO(i), the dK waves read dO(i) and Q(i),
+// and the loads of Q(i + 2) and dO(i + 1) are in flight.  P goes from the dV to
+// the dK waves through two buffers for the same reason.
+template <int D>
+struct DkdvLds {
+  char *q[3], *d[2];
+  float (*sq[3])[BDATTN_BWD_BM];   // per Q tile: -LSE log2(e), lo, hi of its rows
+  float *sd[2];                    // per dO tile: delta of its rows
+  f32x4 *pb[2];                    // P of one tile: [wave pair][half][register quad][lane]
+};
+
+// The loop of one dkdv role.  Per iteration i (one query tile of one head), with
+// P(i) made by the dV waves in iteration i - 1 and left in LDS:
+//   role 0 (dV waves, hold K): S = Q(i+1) K^T and P(i+1) = exp(S - LSE) on the
+//            legal pairs, stored to LDS (fp32, C-register layout) and kept in
+//            registers as bf16; dV^T += dO(i)^T P(i) from the registers.
+//   role 1 (dK waves, hold V): dP = dO(i) V^T; P(i) from LDS (same lane <-> key
+//            map); dS = P o (dP - delta), dK^T += Q(i)^T dS.
+// The roles share no data inside an iteration, so one barrier per iteration
+// suffices and the two waves of a SIMD keep its MFMA unit busy in turn.
 template <int D, int ROLE>
 __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int lb, int le, int kvh,
-                                          int wave, int lane, char *qs0, char *ds0, char *qs1, char *ds1,
-                                          float (*side0)[BDATTN_BWD_BM], float (*side1)[BDATTN_BWD_BM],
-                                          f32x4 *pbuf) {
+                                          int wave, int lane, const DkdvLds<D> &L) {
   constexpr int BM = BDATTN_BWD_BM;
   constexpr int NW = 2 * BDATTN_BWD_WAVES;
   constexpr int NC = D / 16, ND = D / 32;
-  constexpr int VMT = 2 * Tile<D>::LOADS / NW;   // tile loads per wave per iteration
   const int j = lane & 31, g = lane >> 5;
   const int kw = wave & 3;
   const int key = k0 + kw * 32 + j;
@@ -76,94 +86,130 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   f32x16 acc[ND];   // dV^T (role 0) or dK^T (role 1): [head dim][32 keys]
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) acc[dt] = zero_f32x16();
-  // this wave pair's P slot: [half][register quad][lane] of f32x4
-  f32x4 *pslot = pbuf + kw * (2 * 4 * 64);
+  const int pofs = kw * (2 * 4 * 64);   // this wave pair's slot in a P buffer
 
-  const int n_iter = (le - lb) * G;
+  const int n = (le - lb) * G;          // tiles: list entry lb + t / G, head kvh * G + t % G
   const int q_stride = a.h_q * D;
-  auto issue = [&](int it, char *qd, char *dd, float (*side)[BM]) {
-    const int e = lb + it / G, h = kvh * G + it % G;
-    const int qti = ld_table(a.list, e) & 0x7fffffff;
-    const int q0 = ld_table(a.bq, (int64_t)qti * 12), nrows = ld_table(a.bq, (int64_t)qti * 12 + 1);
-    const int64_t off = (int64_t)q0 * q_stride + (int64_t)h * D;
-    tile_load<D, NW>(qd, (const bf16 *)a.q + off, q_stride, nrows, wave, lane);
-    tile_load<D, NW>(dd, (const bf16 *)a.dout + off, q_stride, nrows, wave, lane);
-    if constexpr (ROLE == 0) {   // waves 0..3 also fetch the side rows: lse, delta, lo, hi
-      const int r = q0 + (lane < nrows ? lane : nrows - 1);
-      const void *src;
-      if (wave == 0) src = a.lse + (int64_t)h * a.n_q + r;
-      else if (wave == 1) src = a.delta + (int64_t)h * a.n_q + r;
-      else src = a.rows + (int64_t)r * 4 + 2 * s + (wave - 2);
-      __builtin_amdgcn_global_load_lds(src, BD_LDS(&side[wave][0]), 4, 0, 0);
+  struct TileRef { int q0, nrows, full, h; };
+  auto tile = [&](int t) {
+    const int e = lb + t / G;
+    const int ent = ld_table(a.list, e);
+    const int qti = ent & 0x7fffffff;
+    TileRef r;
+    r.q0 = ld_table(a.bq, (int64_t)qti * 12);
+    r.nrows = ld_table(a.bq, (int64_t)qti * 12 + 1);
+    r.full = ent < 0;
+    r.h = kvh * G + t % G;
+    return r;
+  };
+  // Q tile t (+ lo, hi of its rows, by waves 2 and 3) into Q buffer b.  Wave 0
+  // fetches the rows' LSE into a register; lse_store() later puts the exponent
+  // offset -LSE log2(e) into the side rows (FLT_MAX for a row without keys,
+  // LSE = -inf, so that exp2(-inf + offset) is still 0).
+  float lse_reg = 0.f;
+  auto issue_q = [&](int t, int b) {
+    const TileRef r = tile(t);
+    const int64_t off = (int64_t)r.q0 * q_stride + (int64_t)r.h * D;
+    tile_load<D, NW>(L.q[b], (const bf16 *)a.q + off, q_stride, r.nrows, wave, lane);
+    const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
+    if (wave == 0) {
+      lse_reg = a.lse[(int64_t)r.h * a.n_q + row];
+    } else if (wave == 2 || wave == 3) {
+      __builtin_amdgcn_global_load_lds(a.rows + (int64_t)row * 4 + 2 * s + (wave - 2), BD_LDS(&L.sq[b][wave - 1][0]),
+                                       4, 0, 0);
     }
   };
-  // wait until this wave's loads of the current tile landed; the next tile's stay in flight
-  auto wait_current = [&](bool next_issued) {
-    if (!next_issued) wait_vmcnt<0>();
-    else if constexpr (ROLE == 0) wait_vmcnt<VMT + 1>();
-    else wait_vmcnt<VMT>();
+  auto lse_store = [&](int b) {   // wave 0, once its loads have landed
+    if (wave == 0) L.sq[b][0][lane] = fminf(-lse_reg * kLog2e, FLT_MAX);
+  };
+  // dO tile t (+ delta of its rows, by wave 1) into dO buffer b.
+  auto issue_d = [&](int t, int b) {
+    const TileRef r = tile(t);
+    const int64_t off = (int64_t)r.q0 * q_stride + (int64_t)r.h * D;
+    tile_load<D, NW>(L.d[b], (const bf16 *)a.dout + off, q_stride, r.nrows, wave, lane);
+    if (wave == 1) {
+      const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
+      __builtin_amdgcn_global_load_lds(a.delta + (int64_t)r.h * a.n_q + row, BD_LDS(L.sd[b]), 4, 0, 0);
+    }
   };
 
-  // dV waves: P of one 32-row half.  MASKED: the tile holds masked pairs or rows
-  // past the end; each pair is checked against its row's legal key range (a row
-  // without keys has LSE = -inf and gets P = 0).  Unmasked tiles only hold rows
-  // that attend every key of the tile, whose merged LSE is finite.
-  auto make_p = [&](auto masked_tag, int t, int nrows, const char *q_lds, const float (*side)[BM]) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 sc = zero_f32x16();
+  // dV waves, first half of P(t): S = Q K^T from Q buffer bq.  A masked tile
+  // (masked pairs, or rows past the end) gets S = -inf on the illegal pairs, so
+  // that their P is 0; this branch is rare and kept apart from the exponentials.
+  f32x16 sc[2];
+  auto score_tile = [&](int t, int bq) {
+    const TileRef r = tile(t);
+    const char *q_lds = L.q[bq];
+    const float(*side)[BM] = L.sq[bq];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sc = mfma32(rd(q_lds, t, c), kvf[c], sc);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      sc[h2] = zero_f32x16();
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int qb = 32 * t + 8 * s4 + 4 * g;          // rows qb .. qb + 3 of this lane
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&side[0][qb]);
-      f32x4 p4;
-      if constexpr (MASKED) {
-        const u32x4 lo4 = *reinterpret_cast<const u32x4 *>(&side[2][qb]);
-        const u32x4 hi4 = *reinterpret_cast<const u32x4 *>(&side[3][qb]);
-        const int left = nrows - qb;                     // rows qb + i with i < left exist
+      for (int c = 0; c < NC; ++c) sc[h2] = mfma32(rd(q_lds, h2, c), kvf[c], sc[h2]);
+    }
+    if (!r.full || r.nrows < BM) {
+      keep_branch();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(fmaf(sc[4 * s4 + i], a.scale_log2, -l4[i] * kLog2e));
-          const bool ok = (i < left) & (key >= (int)lo4[i]) & (key < (int)hi4[i]);
-          p4[i] = ok ? pv : 0.f;
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int qb = 32 * h2 + 8 * s4 + 4 * g;       // rows qb .. qb + 3 of this lane
+          const u32x4 lo4 = *reinterpret_cast<const u32x4 *>(&side[1][qb]);
+          const u32x4 hi4 = *reinterpret_cast<const u32x4 *>(&side[2][qb]);
+          const int left = r.nrows - qb;                  // rows qb + i with i < left exist
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = (i < left) & (key >= (int)lo4[i]) & (key < (int)hi4[i]);
+            if (!ok) sc[h2][4 * s4 + i] = -INFINITY;
+          }
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(fmaf(sc[4 * s4 + i], a.scale_log2, -l4[i] * kLog2e));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * s4 + i] = p4[i];
-      pslot[(t * 4 + s4) * 64 + lane] = p4;
     }
-    return sc;
+  };
+  // dV waves, second half: P = exp2(S scale log2(e) - LSE log2(e)) (the offset
+  // from the side rows of Q buffer bq) into P buffer bp (fp32) and into pk (bf16
+  // B operands for the dV MFMAs).
+  bf16x8 pk[4];   // [half][16-chunk]
+  auto exp_tile = [&](int bq, int bp) {
+    f32x4 *pslot = L.pb[bp] + pofs;
+    const float *nls = L.sq[bq][0];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const f32x4 nl4 = *reinterpret_cast<const f32x4 *>(&nls[32 * h2 + 8 * s4 + 4 * g]);
+        f32x4 p4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(fmaf(sc[h2][4 * s4 + i], a.scale_log2, nl4[i]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[h2][4 * s4 + i] = p4[i];
+        pslot[(h2 * 4 + s4) * 64 + lane] = p4;
+      }
+      pk[2 * h2] = pack8(sc[h2], 0);
+      pk[2 * h2 + 1] = pack8(sc[h2], 8);
+    }
   };
 
-  auto compute = [&](int it, const char *q_lds, const char *d_lds, const float (*side)[BM]) {
+  // iteration i with buffers fixed at compile time: K = i mod 6
+  auto step = [&](auto kc, int i) {
+    constexpr int K = decltype(kc)::value;
+    wg_barrier();   // P(i) is in LDS; the buffers of iteration i - 1 are free
+    if (i + 2 < n) issue_q(i + 2, (K + 2) % 3);
+    if (i + 1 < n) issue_d(i + 1, (K + 1) % 2);
     if constexpr (ROLE == 0) {
-      const int e = lb + it / G;
-      const int ent = ld_table(a.list, e);
-      const int nrows = ld_table(a.bq, (int64_t)(ent & 0x7fffffff) * 12 + 1);
-      f32x16 p0, p1;
-      if (ent >= 0 || nrows < BM) {   // partial key range, or a ragged query tile
-        p0 = make_p(std::true_type{}, 0, nrows, q_lds, side);
-        p1 = make_p(std::true_type{}, 1, nrows, q_lds, side);
-      } else {
-        p0 = make_p(std::false_type{}, 0, nrows, q_lds, side);
-        p1 = make_p(std::false_type{}, 1, nrows, q_lds, side);
-      }
-      wait_lgkm0();
-      wg_barrier();
-      // dV^T += dO^T P
+      // S of tile i + 1 (of tile n - 1 again in the last iteration: computed, unused)
+      const bf16x8 pb[4] = {pk[0], pk[1], pk[2], pk[3]};
+      score_tile(min(i + 1, n - 1), (K + 1) % 3);
+      // dV^T += dO(i)^T P(i), independent of the exponentials of P(i + 1)
+      const char *d_lds = L.d[K % 2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int c16 = 0; c16 < 4; ++c16)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 pb = pack8(t == 0 ? p0 : p1, 8 * cc);
-#pragma unroll
-          for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(tr(d_lds, 2 * t + cc, dt), pb, acc[dt]);
-        }
+        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(tr(d_lds, c16, dt), pb[c16], acc[dt]);
+      exp_tile((K + 1) % 3, (K + 1) % 2);
     } else {
+      const char *d_lds = L.d[K % 2], *q_lds = L.q[K % 3];
+      const f32x4 *pslot = L.pb[K % 2] + pofs;
+      const float *dl = L.sd[K % 2];
       f32x16 dp[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -171,17 +217,15 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
 #pragma unroll
         for (int c = 0; c < NC; ++c) dp[t] = mfma32(rd(d_lds, t, c), kvf[c], dp[t]);
       }
-      wait_lgkm0();
-      wg_barrier();
       // dS = P o (dP - delta); dK^T += Q^T dS
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const f32x4 p4 = pslot[(t * 4 + s4) * 64 + lane];
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&side[1][32 * t + 8 * s4 + 4 * g]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl[32 * t + 8 * s4 + 4 * g]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dp[t][4 * s4 + i] = p4[i] * (dp[t][4 * s4 + i] - d4[i]);
+          for (int ii = 0; ii < 4; ++ii) dp[t][4 * s4 + ii] = p4[ii] * (dp[t][4 * s4 + ii] - d4[ii]);
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
@@ -191,24 +235,35 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
         }
       }
     }
+    wait_vmcnt<0>();
+    if (i + 2 < n) lse_store((K + 2) % 3);
+    wait_lgkm0();
   };
 
-  if (n_iter > 0) issue(0, qs0, ds0, side0);
-  for (int it = 0; it < n_iter; it += 2) {
-    if (it + 1 < n_iter) issue(it + 1, qs1, ds1, side1);
-    wait_current(it + 1 < n_iter);
-    wg_barrier();
-    compute(it, qs0, ds0, side0);
+  if (n > 0) {
+    // prologue: Q(0), Q(1), dO(0) and their side rows; P(0)
+    issue_q(0, 0);
+    wait_vmcnt<0>();
+    lse_store(0);
+    issue_d(0, 0);
+    if (n > 1) issue_q(1, 1);
+    wait_vmcnt<0>();
+    if (n > 1) lse_store(1);
     wait_lgkm0();
     wg_barrier();
-    if (it + 1 < n_iter) {
-      if (it + 2 < n_iter) issue(it + 2, qs0, ds0, side0);
-      wait_current(it + 2 < n_iter);
-      wg_barrier();
-      compute(it + 1, qs1, ds1, side1);
-      wait_lgkm0();
-      wg_barrier();
+    if constexpr (ROLE == 0) {
+      score_tile(0, 0);
+      exp_tile(0, 0);
     }
+    wait_lgkm0();
+  }
+  for (int i = 0; i < n; i += 6) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n) step(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 < n) step(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 < n) step(std::integral_constant<int, 3>{}, i + 3);
+    if (i + 4 < n) step(std::integral_constant<int, 4>{}, i + 4);
+    if (i + 5 < n) step(std::integral_constant<int, 5>{}, i + 5);
   }
 
   if (!kvalid) return;
@@ -231,20 +286,24 @@ __global__ __launch_bounds__(2 * 256, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int BM = BDATTN_BWD_BM;
   static_assert(BM == Tile<D>::ROWS, "query tile = one LDS tile");
   __shared__ __attribute__((aligned(1024))) char qs0[Tile<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char ds0[Tile<D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char qs1[Tile<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qs2[Tile<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char ds0[Tile<D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char ds1[Tile<D>::BYTES];
-  // per query row of the tile: lse, delta, legal key range lo, hi
-  __shared__ __attribute__((aligned(16))) float side0[4][BM];
-  __shared__ __attribute__((aligned(16))) float side1[4][BM];
-  // P of the current tile, handed from the dV waves to the dK waves
-  __shared__ f32x4 pbuf[4 * 2 * 4 * 64];
+  __shared__ __attribute__((aligned(16))) float sq0[3][BM];
+  __shared__ __attribute__((aligned(16))) float sq1[3][BM];
+  __shared__ __attribute__((aligned(16))) float sq2[3][BM];
+  __shared__ __attribute__((aligned(16))) float sd0[BM];
+  __shared__ __attribute__((aligned(16))) float sd1[BM];
+  __shared__ f32x4 pb0[4 * 2 * 4 * 64];
+  __shared__ f32x4 pb1[4 * 2 * 4 * 64];
+  const DkdvLds<D> L = {{qs0, qs1, qs2}, {ds0, ds1}, {sq0, sq1, sq2}, {sd0, sd1}, {pb0, pb1}};
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int kti = blockIdx.x / a.h_kv, kvh = blockIdx.x % a.h_kv;
   const int s = ld_table(a.ktiles, (int64_t)kti * 4), k0 = ld_table(a.ktiles, (int64_t)kti * 4 + 1);
   const int lb = ld_table(a.ktiles, (int64_t)kti * 4 + 2), le = ld_table(a.ktiles, (int64_t)kti * 4 + 3);
-  if (wave < 4) dkdv_role<D, 0>(a, s, k0, lb, le, kvh, wave, lane, qs0, ds0, qs1, ds1, side0, side1, pbuf);
-  else dkdv_role<D, 1>(a, s, k0, lb, le, kvh, wave, lane, qs0, ds0, qs1, ds1, side0, side1, pbuf);
+  if (wave < 4) dkdv_role<D, 0>(a, s, k0, lb, le, kvh, wave, lane, L);
+  else dkdv_role<D, 1>(a, s, k0, lb, le, kvh, wave, lane, L);
 }
 
 template <int D>
