@@ -11,11 +11,16 @@ and 10d in the backward (QK^T recompute, dO V^T, P^T dO, dS^T Q, dS K).
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 
 Prints one JSON line.  --gpus N with N > 1 is refused: this path runs on one GPU.
+
+The roofline entry's "traffic" (HBM bytes per launch of the dK/dV kernel) comes
+from rocprofv3 FETCH_SIZE and WRITE_SIZE passes recorded in profiles/; it is
+reported only while the kernel sources still hash to the profiled ones.
 """
 from __future__ import annotations
 
 import argparse
 import contextlib
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +33,31 @@ if ROOT not in sys.path:
 METRIC = "BDLM attention fwd+bwd useful-pair TFLOP/s and % bf16 MFMA peak, 256K/rank"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "dkdv_kernel_256K_rank_share_hbm_traffic.md")
+KERNEL_SOURCES = ["masked_long_context_amd/csrc/tiling.h", "masked_long_context_amd/csrc/kernels/bwd.hip",
+                  "masked_long_context_amd/csrc/kernels/common.h", "masked_long_context_amd/csrc/kernels/kernels.h",
+                  "masked_long_context_amd/csrc/kernels/lds_layout.h", "masked_long_context_amd/csrc/kernels/tiles.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per dK/dV launch from the committed counter summary, or None when
+    the summary is missing, covers another workload, or the kernel changed since."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(l.strip("` \n").split(" = ", 1) for l in f if l.startswith("`") and " = " in l)
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256") != kernel_source_hash() or kv.get("workload") != workload:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 class EventTimer:
@@ -83,6 +113,33 @@ def cpu_baseline_bdlm(cfg, inp_cpu, n_rows: int, seed: int = 0):
     return dt, pairs, len(rows)
 
 
+def merge_microbench(p, n_parts: int = 16, reps: int = 5):
+    """LSE merge of n_parts synthetic fp32 partials of the rank's shape: O ~ N(0, 1),
+    LSE ~ U(0, 15), 10% of the (head, row) entries -inf; bf16 output."""
+    import torch
+    from masked_long_context_amd import bdattn
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    o_parts = torch.randn((n_parts, p.n_q, p.h_q, p.head_dim), generator=gen, device="cuda", dtype=torch.float32)
+    lse_parts = torch.rand((n_parts, p.h_q, p.n_q), generator=gen, device="cuda") * 15.0
+    lse_parts[torch.rand((n_parts, p.h_q, p.n_q), generator=gen, device="cuda") < 0.1] = float("-inf")
+    o = torch.empty((p.n_q, p.h_q, p.head_dim), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((p.h_q, p.n_q), device="cuda", dtype=torch.float32)
+    bdattn.bdattn_lse_merge(o_parts, lse_parts, o, lse)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        bdattn.bdattn_lse_merge(o_parts, lse_parts, o, lse)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = p.n_q * p.h_q * (n_parts * (4 * p.head_dim + 4) + (2 * p.head_dim + 4))
+    del o_parts, lse_parts
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"parts": n_parts, "ms": round(ms, 4), "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -95,11 +152,11 @@ def blas_threads():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -157,6 +214,7 @@ def main():
     merge_ms, merge_n = tot.get("merge", (0.0, 1))
     merge_bytes = p.n_q * p.h_q * (n_act * (4 * p.head_dim + 4) + (2 * p.head_dim + 4))
     merge_gbs = merge_bytes / (merge_ms / merge_n * 1e-3) / 1e9 if merge_ms else 0.0
+    merge_micro = merge_microbench(p)
     if args.copy_calibration:
         # a plain copy of known size, for scaling HBM counters read by rocprofv3
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -176,12 +234,13 @@ def main():
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": f"dkdv_kernel<{p.head_dim}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "ms_per_launch": round(dk["ms_per_launch"], 4),
+                     "traffic": profiled_traffic(cfg.name), "ms_per_launch": round(dk["ms_per_launch"], 4),
                      "flops_per_launch": dk_flops_per_launch},
         "kernels": {
             **{k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
             "merge": {"ms": round(merge_ms / max(merge_n, 1), 4), "parts": n_act, "gbs": round(merge_gbs, 1),
                       "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4)},
+            "merge_micro": merge_micro,
             "prepare_ms": round(tot.get("prepare", (0.0, 1))[0] / args.steps, 4),
             "finalize_ms": round(tot.get("finalize", (0.0, 1))[0] / args.steps, 4),
         },
