@@ -183,6 +183,7 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   a.bq = img(ws, p.hdr.off_bq);
   a.ktiles = img(ws, p.hdr.off_kt);
   a.list = img(ws, p.hdr.off_list);
+  a.lrec = img(ws, p.hdr.off_lrec);
   a.n_items = rows ? p.hdr.n_fwd : 0;
   a.n_kt = p.hdr.n_kt;
   a.n_bq = p.hdr.n_bq;

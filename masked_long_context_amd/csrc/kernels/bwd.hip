@@ -49,68 +49,86 @@ struct DkdvLds {
   char *q[3], *d[2];
   float (*sq[3])[BDATTN_BWD_BM];   // per Q tile: -LSE log2(e), lo, hi of its rows
   float *sd[2];                    // per dO tile: delta of its rows
-  f32x4 *pb[2];                    // P of one tile: [wave pair][half][register quad][lane]
+  f32x4 *pb[2];                    // P of one tile: [wave][row half][key tile][register quad][lane]
 };
 
-// The loop of one dkdv role.  Per iteration i (one query tile of one head), with
-// P(i) made by the dV waves in iteration i - 1 and left in LDS:
+// The loop of one dkdv role.  A wave owns KT column tiles of 32 keys, so every
+// Q or dO operand it reads from LDS feeds KT MFMAs.  Per iteration i (one query
+// tile of one head), with P(i) made by the dV waves in iteration i - 1 and left
+// in LDS:
 //   role 0 (dV waves, hold K): S = Q(i+1) K^T and P(i+1) = exp(S - LSE) on the
 //            legal pairs, stored to LDS (fp32, C-register layout) and kept in
 //            registers as bf16; dV^T += dO(i)^T P(i) from the registers.
 //   role 1 (dK waves, hold V): dP = dO(i) V^T; P(i) from LDS (same lane <-> key
 //            map); dS = P o (dP - delta), dK^T += Q(i)^T dS.
 // The roles share no data inside an iteration, so one barrier per iteration
-// suffices and the two waves of a SIMD keep its MFMA unit busy in turn.
-template <int D, int ROLE>
+// suffices.
+template <int D, int KT, int ROLE>
 __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int lb, int le, int kvh,
                                           int wave, int lane, const DkdvLds<D> &L) {
   constexpr int BM = BDATTN_BWD_BM;
-  constexpr int NW = 2 * BDATTN_BWD_WAVES;
+  constexpr int NWR = 4 / KT;   // waves per role
   constexpr int NC = D / 16, ND = D / 32;
   const int j = lane & 31, g = lane >> 5;
-  const int kw = wave & 3;
-  const int key = k0 + kw * 32 + j;
-  const bool kvalid = key < a.n_seg[s];
+  const int kw = wave % NWR;
+  int key[KT];
+  bool kvalid[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    key[kt] = k0 + (kw * KT + kt) * 32 + j;
+    kvalid[kt] = key[kt] < a.n_seg[s];
+  }
   const int G = a.group;
 
-  // K (dV waves) or V (dK waves) as the B operand (lane = key column, k = head dim).
-  bf16x8 kvf[NC];
-  {
-    const int64_t off = ((int64_t)(kvalid ? key : 0) * a.h_kv + kvh) * D;
+  // K (dV waves) or V (dK waves) as B operands (lane = key column, k = head dim).
+  bf16x8 kvf[KT][NC];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int64_t off = ((int64_t)(kvalid[kt] ? key[kt] : 0) * a.h_kv + kvh) * D;
     const bf16 *src = (const bf16 *)(ROLE == 0 ? a.k[s] : a.v[s]) + off;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kvf[c] = kvalid ? ld_bf16x8(src + 16 * c + 8 * g) : zero_bf16x8();
+    for (int c = 0; c < NC; ++c) kvf[kt][c] = kvalid[kt] ? ld_bf16x8(src + 16 * c + 8 * g) : zero_bf16x8();
   }
   const RowReader<D> rd(lane);
   const TrReader<D> tr(lane);
-  f32x16 acc[ND];   // dV^T (role 0) or dK^T (role 1): [head dim][32 keys]
+  f32x16 acc[ND][KT];   // dV^T (role 0) or dK^T (role 1): [head dim][keys]
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) acc[dt] = zero_f32x16();
-  const int pofs = kw * (2 * 4 * 64);   // this wave pair's slot in a P buffer
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) acc[dt][kt] = zero_f32x16();
+  const int pofs = kw * (2 * KT * 4 * 64);   // this wave pair's slot in a P buffer
+  auto pidx = [&](int h2, int kt, int s4) { return pofs + ((h2 * KT + kt) * 4 + s4) * 64 + lane; };
 
   const int n = (le - lb) * G;          // tiles: list entry lb + t / G, head kvh * G + t % G
   const int q_stride = a.h_q * D;
+  // Tile t's list entry record {q0, rows, full, q-tile} (a scalar load; t is
+  // clamped to n - 1, so the entry stays inside this key tile's list).  Records
+  // are fetched a full iteration before their tiles are used, which hides the
+  // scalar load's latency.
   struct TileRef { int q0, nrows, full, h; };
-  auto tile = [&](int t) {
-    const int e = lb + t / G;
-    const int ent = ld_table(a.list, e);
-    const int qti = ent & 0x7fffffff;
-    TileRef r;
-    r.q0 = ld_table(a.bq, (int64_t)qti * 12);
-    r.nrows = ld_table(a.bq, (int64_t)qti * 12 + 1);
-    r.full = ent < 0;
-    r.h = kvh * G + t % G;
-    return r;
+  const u32x4 *lrec = reinterpret_cast<const u32x4 *>(a.lrec);
+  auto fetch = [&](int t) { return ld_table(lrec, lb + min(t, n - 1) / G); };
+  auto ref = [&](const u32x4 &r, int t) {
+    TileRef x;
+    x.q0 = (int)r[0];
+    x.nrows = (int)r[1];
+    x.full = (int)r[2];
+    x.h = kvh * G + min(t, n - 1) % G;
+    return x;
   };
-  // Q tile t (+ lo, hi of its rows, by waves 2 and 3) into Q buffer b.  Wave 0
-  // fetches the rows' LSE into a register; lse_store() later puts the exponent
+  u32x4 rec1 = {0u, 0u, 0u, 0u}, rec2 = {0u, 0u, 0u, 0u};   // records of tiles i + 1 and i + 2
+  // Loads of iteration i: Q(i + 2) and dO(i + 1), each with side rows.  The side
+  // rows (one dword per lane) are issued at the start of the iteration.  Wave 0
+  // fetches the Q tile's LSE into a register; lse_store() later puts the exponent
   // offset -LSE log2(e) into the side rows (FLT_MAX for a row without keys,
-  // LSE = -inf, so that exp2(-inf + offset) is still 0).
+  // LSE = -inf, so that exp2(-inf + offset) is still 0).  Waves 2 and 3 fetch the
+  // rows' legal key bounds, wave 1 the dO tile's delta.  The tile loads (1 KB per
+  // instruction) are issued by the dK waves alone: a wave stalls at issue until
+  // the CU's vector memory path accepts its loads, and the dK waves have the
+  // slack (their iteration is shorter than the dV waves', which carry the
+  // exponentials).
   float lse_reg = 0.f;
-  auto issue_q = [&](int t, int b) {
-    const TileRef r = tile(t);
-    const int64_t off = (int64_t)r.q0 * q_stride + (int64_t)r.h * D;
-    tile_load<D, NW>(L.q[b], (const bf16 *)a.q + off, q_stride, r.nrows, wave, lane);
+  auto side_q = [&](const TileRef &r, int b) {
     const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
     if (wave == 0) {
       lse_reg = a.lse[(int64_t)r.h * a.n_q + row];
@@ -122,30 +140,42 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   auto lse_store = [&](int b) {   // wave 0, once its loads have landed
     if (wave == 0) L.sq[b][0][lane] = fminf(-lse_reg * kLog2e, FLT_MAX);
   };
-  // dO tile t (+ delta of its rows, by wave 1) into dO buffer b.
-  auto issue_d = [&](int t, int b) {
-    const TileRef r = tile(t);
-    const int64_t off = (int64_t)r.q0 * q_stride + (int64_t)r.h * D;
-    tile_load<D, NW>(L.d[b], (const bf16 *)a.dout + off, q_stride, r.nrows, wave, lane);
+  auto side_d = [&](const TileRef &r, int b) {
     if (wave == 1) {
       const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
       __builtin_amdgcn_global_load_lds(a.delta + (int64_t)r.h * a.n_q + row, BD_LDS(L.sd[b]), 4, 0, 0);
+    }
+  };
+  auto tile_q = [&](const TileRef &r, int b) {
+    if constexpr (ROLE == 1) {
+      const int64_t off = (int64_t)r.q0 * q_stride + (int64_t)r.h * D;
+      tile_load<D, NWR>(L.q[b], (const bf16 *)a.q + off, q_stride, r.nrows, wave - NWR, lane);
+    }
+  };
+  auto tile_d = [&](const TileRef &r, int b) {
+    if constexpr (ROLE == 1) {
+      const int64_t off = (int64_t)r.q0 * q_stride + (int64_t)r.h * D;
+      tile_load<D, NWR>(L.d[b], (const bf16 *)a.dout + off, q_stride, r.nrows, wave - NWR, lane);
     }
   };
 
   // dV waves, first half of P(t): S = Q K^T from Q buffer bq.  A masked tile
   // (masked pairs, or rows past the end) gets S = -inf on the illegal pairs, so
   // that their P is 0; this branch is rare and kept apart from the exponentials.
-  f32x16 sc[2];
-  auto score_tile = [&](int t, int bq) {
-    const TileRef r = tile(t);
+  f32x16 sc[2][KT];
+  auto score_tile = [&](const TileRef &r, int bq) {
     const char *q_lds = L.q[bq];
     const float(*side)[BM] = L.sq[bq];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      sc[h2] = zero_f32x16();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sc[h2] = mfma32(rd(q_lds, h2, c), kvf[c], sc[h2]);
+      for (int kt = 0; kt < KT; ++kt) sc[h2][kt] = zero_f32x16();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 qa = rd(q_lds, h2, c);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) sc[h2][kt] = mfma32(qa, kvf[kt][c], sc[h2][kt]);
+      }
     }
     if (!r.full || r.nrows < BM) {
       keep_branch();
@@ -158,34 +188,42 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
           const u32x4 hi4 = *reinterpret_cast<const u32x4 *>(&side[2][qb]);
           const int left = r.nrows - qb;                  // rows qb + i with i < left exist
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = (i < left) & (key >= (int)lo4[i]) & (key < (int)hi4[i]);
-            if (!ok) sc[h2][4 * s4 + i] = -INFINITY;
-          }
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool ok = (i < left) & (key[kt] >= (int)lo4[i]) & (key[kt] < (int)hi4[i]);
+              if (!ok) sc[h2][kt][4 * s4 + i] = -INFINITY;
+            }
         }
     }
   };
   // dV waves, second half: P = exp2(S scale log2(e) - LSE log2(e)) (the offset
   // from the side rows of Q buffer bq) into P buffer bp (fp32) and into pk (bf16
   // B operands for the dV MFMAs).
-  bf16x8 pk[4];   // [half][16-chunk]
+  bf16x8 pk[4][KT];   // [16-row chunk][key tile]
   auto exp_tile = [&](int bq, int bp) {
-    f32x4 *pslot = L.pb[bp] + pofs;
+    f32x4 *pbuf = L.pb[bp];
     const float *nls = L.sq[bq][0];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const f32x4 nl4 = *reinterpret_cast<const f32x4 *>(&nls[32 * h2 + 8 * s4 + 4 * g]);
-        f32x4 p4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(fmaf(sc[h2][4 * s4 + i], a.scale_log2, nl4[i]));
+        for (int kt = 0; kt < KT; ++kt) {
+          f32x4 p4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[h2][4 * s4 + i] = p4[i];
-        pslot[(h2 * 4 + s4) * 64 + lane] = p4;
+          for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(fmaf(sc[h2][kt][4 * s4 + i], a.scale_log2, nl4[i]));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[h2][kt][4 * s4 + i] = p4[i];
+          pbuf[pidx(h2, kt, s4)] = p4;
+        }
       }
-      pk[2 * h2] = pack8(sc[h2], 0);
-      pk[2 * h2 + 1] = pack8(sc[h2], 8);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        pk[2 * h2][kt] = pack8(sc[h2][kt], 0);
+        pk[2 * h2 + 1][kt] = pack8(sc[h2][kt], 8);
+      }
     }
   };
 
@@ -193,66 +231,109 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   auto step = [&](auto kc, int i) {
     constexpr int K = decltype(kc)::value;
     wg_barrier();   // P(i) is in LDS; the buffers of iteration i - 1 are free
-    if (i + 2 < n) issue_q(i + 2, (K + 2) % 3);
-    if (i + 1 < n) issue_d(i + 1, (K + 1) % 2);
+    const bool hq = i + 2 < n, hd = i + 1 < n;
+    const TileRef r1 = ref(rec1, i + 1), r2 = ref(rec2, i + 2);
+    const u32x4 rec3 = fetch(i + 3);
+    if (hq) {
+      side_q(r2, (K + 2) % 3);
+      tile_q(r2, (K + 2) % 3);
+    }
+    if (hd) {
+      side_d(r1, (K + 1) % 2);
+      tile_d(r1, (K + 1) % 2);
+    }
     if constexpr (ROLE == 0) {
       // S of tile i + 1 (of tile n - 1 again in the last iteration: computed, unused)
-      const bf16x8 pb[4] = {pk[0], pk[1], pk[2], pk[3]};
-      score_tile(min(i + 1, n - 1), (K + 1) % 3);
+      bf16x8 pb[4][KT];
+#pragma unroll
+      for (int c16 = 0; c16 < 4; ++c16)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) pb[c16][kt] = pk[c16][kt];
+      score_tile(r1, (K + 1) % 3);
       // dV^T += dO(i)^T P(i), independent of the exponentials of P(i + 1)
       const char *d_lds = L.d[K % 2];
 #pragma unroll
       for (int c16 = 0; c16 < 4; ++c16)
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(tr(d_lds, c16, dt), pb[c16], acc[dt]);
+        for (int dt = 0; dt < ND; ++dt) {
+          const bf16x8 da = tr(d_lds, c16, dt);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) acc[dt][kt] = mfma32(da, pb[c16][kt], acc[dt][kt]);
+        }
       exp_tile((K + 1) % 3, (K + 1) % 2);
     } else {
       const char *d_lds = L.d[K % 2], *q_lds = L.q[K % 3];
-      const f32x4 *pslot = L.pb[K % 2] + pofs;
+      const f32x4 *pbuf = L.pb[K % 2];
       const float *dl = L.sd[K % 2];
-      f32x16 dp[2];
+      f32x16 dp[2][KT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dp[t] = zero_f32x16();
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) dp[t] = mfma32(rd(d_lds, t, c), kvf[c], dp[t]);
+        for (int kt = 0; kt < KT; ++kt) dp[h2][kt] = zero_f32x16();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 da = rd(d_lds, h2, c);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) dp[h2][kt] = mfma32(da, kvf[kt][c], dp[h2][kt]);
+        }
       }
       // dS = P o (dP - delta); dK^T += Q^T dS
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          const f32x4 p4 = pslot[(t * 4 + s4) * 64 + lane];
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl[32 * t + 8 * s4 + 4 * g]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&dl[32 * h2 + 8 * s4 + 4 * g]);
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) dp[t][4 * s4 + ii] = p4[ii] * (dp[t][4 * s4 + ii] - d4[ii]);
+          for (int kt = 0; kt < KT; ++kt) {
+            const f32x4 p4 = pbuf[pidx(h2, kt, s4)];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) dp[h2][kt][4 * s4 + ii] = p4[ii] * (dp[h2][kt][4 * s4 + ii] - d4[ii]);
+          }
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 db = pack8(dp[t], 8 * cc);
+          bf16x8 db[KT];
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt) acc[dt] = mfma32(tr(q_lds, 2 * t + cc, dt), db, acc[dt]);
+          for (int kt = 0; kt < KT; ++kt) db[kt] = pack8(dp[h2][kt], 8 * cc);
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const bf16x8 qa = tr(q_lds, 2 * h2 + cc, dt);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) acc[dt][kt] = mfma32(qa, db[kt], acc[dt][kt]);
+          }
         }
       }
     }
     wait_vmcnt<0>();
     if (i + 2 < n) lse_store((K + 2) % 3);
     wait_lgkm0();
+    rec1 = rec2;
+    rec2 = rec3;
   };
 
   if (n > 0) {
     // prologue: Q(0), Q(1), dO(0) and their side rows; P(0)
-    issue_q(0, 0);
+    const u32x4 rec0 = fetch(0);
+    rec1 = fetch(1);
+    rec2 = fetch(2);
+    const TileRef r0 = ref(rec0, 0);
+    side_q(r0, 0);
+    tile_q(r0, 0);
     wait_vmcnt<0>();
     lse_store(0);
-    issue_d(0, 0);
-    if (n > 1) issue_q(1, 1);
+    side_d(r0, 0);
+    tile_d(r0, 0);
+    if (n > 1) {
+      const TileRef r1 = ref(rec1, 1);
+      side_q(r1, 1);
+      tile_q(r1, 1);
+    }
     wait_vmcnt<0>();
     if (n > 1) lse_store(1);
     wait_lgkm0();
     wg_barrier();
     if constexpr (ROLE == 0) {
-      score_tile(0, 0);
+      score_tile(r0, 0);
       exp_tile(0, 0);
     }
     wait_lgkm0();
@@ -266,23 +347,31 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
     if (i + 5 < n) step(std::integral_constant<int, 5>{}, i + 5);
   }
 
-  if (!kvalid) return;
   const float mul = ROLE == 0 ? 1.f : a.scale;
-  bf16 *outp = (bf16 *)(ROLE == 0 ? a.dv[s] : a.dk[s]) + ((int64_t)key * a.h_kv + kvh) * D;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
+  for (int kt = 0; kt < KT; ++kt) {
+    if (!kvalid[kt]) continue;
+    bf16 *outp = (bf16 *)(ROLE == 0 ? a.dv[s] : a.dk[s]) + ((int64_t)key[kt] * a.h_kv + kvh) * D;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int d0 = 32 * dt + 8 * s4 + 4 * g;
-      bf16x4 b;
+    for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = (bf16)(acc[dt][4 * s4 + i] * mul);
-      *reinterpret_cast<bf16x4 *>(outp + d0) = b;
-    }
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int d0 = 32 * dt + 8 * s4 + 4 * g;
+        bf16x4 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = (bf16)(acc[dt][kt][4 * s4 + i] * mul);
+        *reinterpret_cast<bf16x4 *>(outp + d0) = b;
+      }
+  }
 }
 
+// Key tiles of 32 per wave of the dK/dV kernel (1: 8 waves, 2 per SIMD; 2: 4
+// waves, one per SIMD with the whole register file).
+constexpr int kDkdvKT = 1;
+constexpr int kDkdvThreads = 2 * (4 / kDkdvKT) * 64;
+
 template <int D>
-__global__ __launch_bounds__(2 * 256, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int BM = BDATTN_BWD_BM;
   static_assert(BM == Tile<D>::ROWS, "query tile = one LDS tile");
   __shared__ __attribute__((aligned(1024))) char qs0[Tile<D>::BYTES];
@@ -302,8 +391,8 @@ __global__ __launch_bounds__(2 * 256, 1) void dkdv_kernel(BwdArgs a) {
   const int kti = blockIdx.x / a.h_kv, kvh = blockIdx.x % a.h_kv;
   const int s = ld_table(a.ktiles, (int64_t)kti * 4), k0 = ld_table(a.ktiles, (int64_t)kti * 4 + 1);
   const int lb = ld_table(a.ktiles, (int64_t)kti * 4 + 2), le = ld_table(a.ktiles, (int64_t)kti * 4 + 3);
-  if (wave < 4) dkdv_role<D, 0>(a, s, k0, lb, le, kvh, wave, lane, L);
-  else dkdv_role<D, 1>(a, s, k0, lb, le, kvh, wave, lane, L);
+  if (wave < 4 / kDkdvKT) dkdv_role<D, kDkdvKT, 0>(a, s, k0, lb, le, kvh, wave, lane, L);
+  else dkdv_role<D, kDkdvKT, 1>(a, s, k0, lb, le, kvh, wave, lane, L);
 }
 
 template <int D>
@@ -462,8 +551,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, bool dq) {
   const int64_t kblocks = dkdv ? (int64_t)a.n_kt * a.h_kv : 0;
   if (kblocks > 0) {
-    if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)kblocks), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)kblocks), dim3(512), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)kblocks), dim3(kDkdvThreads), 0, s, a);
+    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)kblocks), dim3(kDkdvThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -30,6 +30,7 @@ struct BwdArgs {
   const int32_t *bq;        // [n_bq][12] query tiles of the dK/dV kernel
   const int32_t *ktiles;    // [n_kt][4]
   const int32_t *list;      // [n_list]
+  const int32_t *lrec;      // [n_list][4] per list entry {q0, rows, full, q-tile}
   int32_t n_items, n_kt, n_bq, n_q, h_q, h_kv, group;
   float scale, scale_log2;
 };

@@ -106,6 +106,14 @@ void build_bwd_lists(Plan &p) {
       }
     }
   }
+  p.lrec.assign(p.list.size() * 4, 0);
+  for (size_t i = 0; i < p.list.size(); ++i) {
+    const int32_t qi = p.list[i] & INT32_MAX;
+    p.lrec[4 * i + 0] = p.bq[qi].q0;
+    p.lrec[4 * i + 1] = p.bq[qi].rows;
+    p.lrec[4 * i + 2] = p.list[i] < 0 ? 1 : 0;
+    p.lrec[4 * i + 3] = qi;
+  }
   p.kt.clear();
   for (int s = 0; s < 2; ++s)
     for (int64_t k = 0; k < nkt[s]; ++k) {
@@ -124,7 +132,7 @@ void finish(Plan &p) {
       p.useful_pairs += std::max<int64_t>(0, (int64_t)p.rows[r * 4 + 2 * s + 1] - p.rows[r * 4 + 2 * s]);
   build_bwd_lists(p);
 
-  // Device image: header | rows | fwd items | bwd q-tiles | bwd k-tiles | bwd list.
+  // Device image: header | rows | fwd items | bwd q-tiles | bwd k-tiles | bwd list | list records.
   ImageHeader &h = p.hdr;
   std::memset(&h, 0, sizeof(h));
   h.magic = BDATTN_IMAGE_MAGIC;
@@ -141,6 +149,7 @@ void finish(Plan &p) {
   h.off_bq = off;    off = align_up(off + (int64_t)p.bq.size() * sizeof(TileDesc), BDATTN_ALIGN);
   h.off_kt = off;    off = align_up(off + (int64_t)p.kt.size() * sizeof(KTile), BDATTN_ALIGN);
   h.off_list = off;  off = align_up(off + (int64_t)p.list.size() * 4, BDATTN_ALIGN);
+  h.off_lrec = off;  off = align_up(off + (int64_t)p.lrec.size() * 4, BDATTN_ALIGN);
   h.image_bytes = off;
   p.image.assign(off, 0);
   std::memcpy(p.image.data(), &h, sizeof(h));
@@ -149,6 +158,7 @@ void finish(Plan &p) {
   if (!p.bq.empty()) std::memcpy(p.image.data() + h.off_bq, p.bq.data(), p.bq.size() * sizeof(TileDesc));
   if (!p.kt.empty()) std::memcpy(p.image.data() + h.off_kt, p.kt.data(), p.kt.size() * sizeof(KTile));
   if (!p.list.empty()) std::memcpy(p.image.data() + h.off_list, p.list.data(), p.list.size() * 4);
+  if (!p.lrec.empty()) std::memcpy(p.image.data() + h.off_lrec, p.lrec.data(), p.lrec.size() * 4);
 
   p.ws_bytes = h.image_bytes;
   p.id = g_next_id.fetch_add(1);

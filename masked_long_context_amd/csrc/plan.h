@@ -21,7 +21,7 @@ static_assert(sizeof(KTile) == 16, "KTile layout");
 
 struct ImageHeader {
   int32_t magic, n_q, n_fwd, n_bq, n_kt, n_list, n_seg0, n_seg1;
-  int64_t off_rows, off_fwd, off_bq, off_kt, off_list, image_bytes;
+  int64_t off_rows, off_fwd, off_bq, off_kt, off_list, off_lrec, image_bytes;
 };
 
 struct Plan {
@@ -36,6 +36,9 @@ struct Plan {
   std::vector<TileDesc> bq;     // backward query tiles (natural order)
   std::vector<KTile> kt;        // backward key tiles, longest list first
   std::vector<int32_t> list;    // q-tile index | full << 31, grouped per key tile
+  // Per list entry {q0, rows, full, q-tile index}: the q-tile fields copied, so
+  // that a key-major kernel needs one scalar load per entry.
+  std::vector<int32_t> lrec;
   int64_t useful_pairs = 0;
   // Device image of the tables (uploaded into the head of each workspace).
   std::vector<uint8_t> image;
