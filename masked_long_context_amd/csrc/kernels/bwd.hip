@@ -167,16 +167,18 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
     const char *q_lds = L.q[bq];
     const float(*side)[BM] = L.sq[bq];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) sc[h2][kt] = zero_f32x16();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
         const bf16x8 qa = rd(q_lds, h2, c);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) sc[h2][kt] = mfma32(qa, kvf[kt][c], sc[h2][kt]);
       }
-    }
+    if constexpr (KT == 1) pipeline_lds_mfma<2 * NC, 1, 4>();
     if (!r.full || r.nrows < BM) {
       keep_branch();
 #pragma unroll
@@ -267,16 +269,17 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
       const float *dl = L.sd[K % 2];
       f32x16 dp[2][KT];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) dp[h2][kt] = zero_f32x16();
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
           const bf16x8 da = rd(d_lds, h2, c);
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) dp[h2][kt] = mfma32(da, kvf[kt][c], dp[h2][kt]);
         }
-      }
       // dS = P o (dP - delta); dK^T += Q^T dS
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -473,12 +476,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     for (int kt = 0; kt < 2; ++kt) {
       sc[kt] = zero_f32x16();
       dp[kt] = zero_f32x16();
+    }
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
         sc[kt] = mfma32(rd(k_lds, kt, c), qf[c], sc[kt]);
         dp[kt] = mfma32(rd(v_lds, kt, c), df[c], dp[kt]);
       }
-    }
+    pipeline_lds_mfma<4 * NC, 1, 4>();
     if (!full) {
       keep_branch();
       // illegal pairs get S = -inf, hence P = 0

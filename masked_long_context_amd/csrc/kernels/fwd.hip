@@ -96,12 +96,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int lo = s ? lo1 : lo0, hi = s ? hi1 : hi0;
     f32x16 sc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sc[kt] = zero_f32x16();
+    for (int kt = 0; kt < 2; ++kt) sc[kt] = zero_f32x16();
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        sc[kt] = mfma32(rd(kt_lds, kt, c), qf[c], sc[kt]);
-    }
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma32(rd(kt_lds, kt, c), qf[c], sc[kt]);
+    pipeline_lds_mfma<2 * NC, 1, 4>();
     if (!full) {
       keep_branch();
       // key k0 + 4 g + o (o an immediate) is legal iff lo <= key < hi

@@ -72,6 +72,23 @@ struct TrReader {
   }
 };
 
+// Orders the current scheduling region so that its LDS reads run ahead of the
+// MFMAs that consume them: AHEAD operands are read first, then each MFMA is
+// followed by the reads of the operand AHEAD positions later.  N MFMAs, each
+// consuming one operand of READS LDS reads.  Without it the scheduler, short of
+// registers, reads each operand just before its MFMA and waits for it there.
+template <int N, int READS, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  static_assert(AHEAD <= N, "lookahead longer than the sequence");
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * READS, 0);
+#pragma unroll
+  for (int k = 0; k < N - AHEAD; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // s_waitcnt with vmcnt(N) and the other counters left free (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
