@@ -263,6 +263,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
           for (int kt = 0; kt < KT; ++kt) acc[dt][kt] = mfma32(da, pb[c16][kt], acc[dt][kt]);
         }
       exp_tile((K + 1) % 3, (K + 1) % 2);
+      if constexpr (KT == 1) pipeline_lds_mfma<4 * ND, 2, 4>();
     } else {
       const char *d_lds = L.d[K % 2], *q_lds = L.q[K % 3];
       const f32x4 *pbuf = L.pb[K % 2];
@@ -306,6 +307,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
           }
         }
       }
+      if constexpr (KT == 1) pipeline_lds_mfma<2 * NC + 4 * ND, 2, 4>();
     }
     wait_vmcnt<0>();
     if (i + 2 < n) lse_store((K + 2) % 3);
