@@ -405,7 +405,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   constexpr int BN = BDATTN_FWD_BN;
   static_assert(BN == Tile<D>::ROWS, "key tile = one LDS tile");
   constexpr int NC = D / 16, ND = D / 32;
-  constexpr int VMN = 2 * Tile<D>::LOADS / BDATTN_FWD_WAVES;
   __shared__ __attribute__((aligned(1024))) char ks0[Tile<D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vs0[Tile<D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char ks1[Tile<D>::BYTES];
@@ -514,29 +513,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
   };
 
+  // One barrier per key tile: after it, tile t has landed for every wave and
+  // every wave is done with tile t - 1, whose buffer then takes tile t + 1.
   issue(0, ks0, vs0);
   for (int t = 0; t < total; t += 2) {
-    if (t + 1 < total) {
-      issue(t + 1, ks1, vs1);
-      wait_vmcnt<VMN>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     wg_barrier();
+    if (t + 1 < total) issue(t + 1, ks1, vs1);
     compute(t, ks0, vs0);
     wait_lgkm0();
-    wg_barrier();
     if (t + 1 < total) {
-      if (t + 2 < total) {
-        issue(t + 2, ks0, vs0);
-        wait_vmcnt<VMN>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      wait_vmcnt<0>();
       wg_barrier();
+      if (t + 2 < total) issue(t + 2, ks0, vs0);
       compute(t + 1, ks1, vs1);
       wait_lgkm0();
-      wg_barrier();
     }
   }
 
