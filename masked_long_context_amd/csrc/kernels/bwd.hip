@@ -21,8 +21,8 @@
 //     and dP put one key per lane, so P and dS feed the accumulating MFMAs
 //     straight from the C registers (dO^T and Q^T come from transpose reads).
 //     dK and dV are summed over the group in registers and written once.
-//   dq_kernel (query-major, shaped like the forward): one workgroup = 128 rows
-//     of one q-head.  S^T = K Q^T and dP^T = V dO^T put one query per lane (its
+//   dq_kernel (query-major, shaped like the forward): one workgroup = 32 rows
+//     per wave of one q-head.  S^T = K Q^T and dP^T = V dO^T put one query per lane (its
 //     LSE and delta are scalars), and dQ^T += K^T dS^T takes dS^T from the C
 //     registers and K^T from transpose reads of the K tile.  dQ is owned by one
 //     workgroup per call: it is added to the fp32 accumulator without atomics.
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void dkdv_kernel(BwdArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void dq_kernel(BwdArgs a) {
   constexpr int BN = BDATTN_FWD_BN;
   static_assert(BN == Tile<D>::ROWS, "key tile = one LDS tile");
   constexpr int NC = D / 16, ND = D / 32;
@@ -557,8 +557,8 @@ hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, boo
   }
   const int64_t qblocks = dq ? (int64_t)a.n_items * a.h_q : 0;
   if (qblocks > 0) {
-    if (d == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)qblocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
+    else hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)qblocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
   }
   return hipGetLastError();
 }

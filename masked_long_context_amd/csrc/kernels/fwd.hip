@@ -8,8 +8,8 @@
 // the range's partial O and its log-sum-exp, so that partials over disjoint
 // ranges merge exactly.
 //
-// One workgroup = 4 waves = 128 query rows of one q-head; each wave owns 32
-// rows.  S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane and 16
+// One workgroup = BDATTN_FWD_WAVES waves (32 query rows each) of one q-head;
+// every key tile it loads serves all its waves.  S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane and 16
 // of its keys in the lane's C registers: the row max needs one exchange across
 // the wave halves and the row sum stays in-lane.  The probabilities go straight
 // from the C registers into O^T += V^T P^T as the B operand; V^T comes from
@@ -26,7 +26,7 @@ namespace bdattn {
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void fwd_kernel(FwdArgs a) {
   constexpr int BN = BDATTN_FWD_BN;
   static_assert(BN == Tile<D>::ROWS, "key tile = one LDS tile");
   constexpr int NC = D / 16, ND = D / 32;
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 hipError_t launch_fwd(const FwdArgs &a, int32_t d, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_items * a.h_q;
   if (blocks == 0) return hipSuccess;
-  if (d == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(fwd_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if (d == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3((unsigned)blocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
+  else hipLaunchKernelGGL(fwd_kernel<64>, dim3((unsigned)blocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
