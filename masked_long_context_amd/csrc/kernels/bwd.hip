@@ -11,21 +11,23 @@
 //
 //   dkdv_kernel (key-major): one workgroup = 128 keys of one KV head.  It walks
 //     the query tiles (64 rows) that attend its keys, for every q-head of the
-//     group; Q and dO stream through double-buffered LDS tiles.  Eight waves,
-//     two per SIMD: four "dV waves" (32 keys each, K in registers) compute
-//     S = Q K^T, P and dV^T += dO^T P; four "dK waves" on the same keys (V in
-//     registers) compute dP = dO V^T, take P from the dV waves through LDS, and
-//     form dS and dK^T += Q^T dS.  Each wave keeps one accumulator and one
-//     operand set, so two waves fit every SIMD and one's exp/VALU work overlaps
-//     the other's MFMAs; the MFMA work per pair is that of a fused kernel.  S
-//     and dP put one key per lane, so P and dS feed the accumulating MFMAs
-//     straight from the C registers (dO^T and Q^T come from transpose reads).
-//     dK and dV are summed over the group in registers and written once.
+//     group.  Eight waves, two per SIMD: four "dV waves" (32 keys each, K in
+//     registers) compute S = Q K^T, P and dV^T += dO^T P; four "dK waves" on
+//     the same keys (V in registers) compute dP = dO V^T, take P from the dV
+//     waves through LDS, and form dS and dK^T += Q^T dS.  The dV waves run one
+//     query tile ahead, so the two roles share no data inside an iteration and
+//     one barrier per tile suffices.  Each wave keeps one accumulator and one
+//     operand set, so two waves fit every SIMD; the MFMA work per pair is that
+//     of a fused kernel.  S and dP put one key per lane, so P and dS feed the
+//     accumulating MFMAs straight from the C registers (dO^T and Q^T come from
+//     transpose reads).  dK and dV are summed over the group in registers and
+//     written once.
 //   dq_kernel (query-major, shaped like the forward): one workgroup = 32 rows
-//     per wave of one q-head.  S^T = K Q^T and dP^T = V dO^T put one query per lane (its
-//     LSE and delta are scalars), and dQ^T += K^T dS^T takes dS^T from the C
-//     registers and K^T from transpose reads of the K tile.  dQ is owned by one
-//     workgroup per call: it is added to the fp32 accumulator without atomics.
+//     per wave of one q-head.  S^T = K Q^T and dP^T = V dO^T put one query per
+//     lane (its LSE and delta are scalars), and dQ^T += K^T dS^T takes dS^T
+//     from the C registers and K^T from transpose reads of the K tile.  dQ is
+//     owned by one workgroup per call: it is added to the fp32 accumulator
+//     without atomics.
 // The split recomputes S and dP once more than a fused kernel, but removes the
 // fp32 atomics a fused key-major kernel needs for dQ (about one per useful pair
 // and head), which the L2 executes far slower than the MFMA work they replace.

@@ -9,12 +9,13 @@
 // ranges merge exactly.
 //
 // One workgroup = BDATTN_FWD_WAVES waves (32 query rows each) of one q-head;
-// every key tile it loads serves all its waves.  S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane and 16
-// of its keys in the lane's C registers: the row max needs one exchange across
-// the wave halves and the row sum stays in-lane.  The probabilities go straight
-// from the C registers into O^T += V^T P^T as the B operand; V^T comes from
-// transpose reads of the row-major V tile.  K and V stream through two LDS
-// buffers filled by direct global->LDS loads while the previous tile computes.
+// every key tile it loads serves all its waves.  S^T = K Q^T
+// (v_mfma_f32_32x32x16_bf16) puts one query per lane and 16 of its keys in the
+// lane's C registers: the row max needs one exchange across the wave halves and
+// the row sum stays in-lane.  The probabilities go straight from the C
+// registers into O^T += V^T P^T as the B operand; V^T comes from transpose reads
+// of the row-major V tile.  K and V stream through two LDS buffers filled by
+// direct global->LDS loads while the previous tile computes.
 // Full key tiles skip the mask; partial tiles compare each key with the row's
 // legal range.  The running max is only raised (rescaling O and l) when it grows
 // by more than 2^8, which keeps every probability below 256.
