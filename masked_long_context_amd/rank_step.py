@@ -115,20 +115,29 @@ class VarlenStep:
         self.dq = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
         self.dk = torch.empty((T, h_kv, head_dim), dtype=torch.bfloat16, device=device)
         self.dv = torch.empty_like(self.dk)
+        self.timer = None      # optional callable(tag) -> context manager around each library call
 
     @property
     def useful_pairs(self) -> int:
         return self.plan.useful_pairs
 
+    def _t(self, tag):
+        import contextlib
+        return self.timer(tag) if self.timer is not None else contextlib.nullcontext()
+
     def forward(self, q, k, v):
-        B.bdattn_varlen_fwd(self.plan, q, k, v, self.o, self.lse, self.ws)
+        with self._t("fwd"):
+            B.bdattn_varlen_fwd(self.plan, q, k, v, self.o, self.lse, self.ws)
         return self.o, self.lse
 
     def backward(self, q, k, v, dout):
-        B.bdattn_bwd_prepare(self.plan, self.o, dout, self.delta, self.dq_acc)
-        B.bdattn_varlen_bwd(self.plan, q, k, v, dout, self.lse, self.delta, self.dq_acc,
-                            self.dk, self.dv, self.ws)
-        B.bdattn_dq_finalize(self.dq_acc, self.dq)
+        with self._t("prepare"):
+            B.bdattn_bwd_prepare(self.plan, self.o, dout, self.delta, self.dq_acc)
+        with self._t("bwd"):
+            B.bdattn_varlen_bwd(self.plan, q, k, v, dout, self.lse, self.delta, self.dq_acc,
+                                self.dk, self.dv, self.ws)
+        with self._t("finalize"):
+            B.bdattn_dq_finalize(self.dq_acc, self.dq)
         return self.dq, self.dk, self.dv
 
     def step(self, q, k, v, dout):
