@@ -26,15 +26,19 @@
 namespace bdattn {
 namespace {
 
+// 64-row LDS tiles of K (and of V) per key step of the forward.
+constexpr int kFwdTiles = 2;
+
 template <int D>
 __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void fwd_kernel(FwdArgs a) {
-  constexpr int BN = BDATTN_FWD_BN;
-  static_assert(BN == Tile<D>::ROWS, "key tile = one LDS tile");
+  constexpr int KB = kFwdTiles;               // 64-row LDS tiles per key step
+  constexpr int BN = KB * Tile<D>::ROWS;       // keys per step
+  constexpr int TB = Tile<D>::BYTES;
   constexpr int NC = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(1024))) char ks0[Tile<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char vs0[Tile<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char ks1[Tile<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char vs1[Tile<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char ks0[KB * TB];
+  __shared__ __attribute__((aligned(1024))) char vs0[KB * TB];
+  __shared__ __attribute__((aligned(1024))) char ks1[KB * TB];
+  __shared__ __attribute__((aligned(1024))) char vs1[KB * TB];
 
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, j = lane & 31, g = lane >> 5;
   const int item = blockIdx.x / a.h_q;
@@ -84,30 +88,40 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
   auto issue = [&](int t, char *kd, char *vd) {
     const int s = t < nt[0] ? 0 : 1;
     const int k0 = s == 0 ? base[0] + t * BN : base[1] + (t - nt[0]) * BN;
-    const int64_t off = (int64_t)k0 * kv_stride + kvh * D;
-    const int nv = a.n_seg[s] - k0;
-    tile_load<D, BDATTN_FWD_WAVES>(kd, (const bf16 *)a.k[s] + off, kv_stride, nv, wave, lane);
-    tile_load<D, BDATTN_FWD_WAVES>(vd, (const bf16 *)a.v[s] + off, kv_stride, nv, wave, lane);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      // a step starts below the segment's end; a later tile of it may not: its
+      // rows then all re-read the last row (and are masked, the step not being full)
+      int r0 = k0 + kb * Tile<D>::ROWS, nv = a.n_seg[s] - r0;
+      if (nv < 1) {
+        r0 = a.n_seg[s] - 1;
+        nv = 1;
+      }
+      const int64_t off = (int64_t)r0 * kv_stride + kvh * D;
+      tile_load<D, BDATTN_FWD_WAVES>(kd + kb * TB, (const bf16 *)a.k[s] + off, kv_stride, nv, wave, lane);
+      tile_load<D, BDATTN_FWD_WAVES>(vd + kb * TB, (const bf16 *)a.v[s] + off, kv_stride, nv, wave, lane);
+    }
   };
   auto compute = [&](int t, const char *kt_lds, const char *vt_lds) {
     const int s = t < nt[0] ? 0 : 1;
     const int k0 = s == 0 ? base[0] + t * BN : base[1] + (t - nt[0]) * BN;
     const bool full = lo_max[s] <= k0 && k0 + BN <= hi_min[s];
     const int lo = s ? lo1 : lo0, hi = s ? hi1 : hi0;
-    f32x16 sc[2];
+    constexpr int NKT = BN / 32;   // 32-key column tiles of the step
+    f32x16 sc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) sc[kt] = zero_f32x16();
+    for (int kt = 0; kt < NKT; ++kt) sc[kt] = zero_f32x16();
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma32(rd(kt_lds, kt, c), qf[c], sc[kt]);
-    pipeline_lds_mfma<2 * NC, 1, 4>();
+      for (int kt = 0; kt < NKT; ++kt) sc[kt] = mfma32(rd(kt_lds + (kt >> 1) * TB, kt & 1, c), qf[c], sc[kt]);
+    pipeline_lds_mfma<NKT * NC, 1, 4>();
     if (!full) {
       keep_branch();
       // key k0 + 4 g + o (o an immediate) is legal iff lo <= key < hi
       const int lo_r = lo - k0 - 4 * g, hi_r = hi - k0 - 4 * g;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int o = kt * 32 + 8 * (r >> 2) + (r & 3);
@@ -116,7 +130,7 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
     const float mb = (m_used == -INFINITY) ? 0.f : m_used;
     float psum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = fast_exp2(fmaf(sc[kt][r], a.scale_log2, -mb));
@@ -146,7 +160,7 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
     for (int c16 = 0; c16 < BN / 16; ++c16) {
       const bf16x8 pb = pack8(sc[c16 >> 1], 8 * (c16 & 1));
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma32(tr(vt_lds, c16, dt), pb, oacc[dt]);
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma32(tr(vt_lds + (c16 >> 2) * TB, c16 & 3, dt), pb, oacc[dt]);
     }
   };
 
