@@ -116,6 +116,39 @@ def varlen_mask_fn(cu_seqlens, causal) -> MaskFn:
     return lambda rows, keys: varlen_mask(cu_seqlens, causal, rows, keys)
 
 
+def task_mask(q_cu: Sequence[int], k_cu: Sequence[int], causal: bool, rows: Optional[np.ndarray] = None,
+              keys: Optional[np.ndarray] = None) -> np.ndarray:
+    """Core-attention tasks that carry their own key context ("Efficient
+    Long-context Language Model Training by Core Attention Disaggregation",
+    English abstract: core attention as a stateless task over token-level shards).
+
+    Task t owns query rows [q_cu[t], q_cu[t+1]) and key rows [k_cu[t], k_cu[t+1]).
+    Key j is legal for row i iff both belong to the same task and, if causal, j is
+    among the first k_len - q_len + i' + 1 keys of the task (i' = the row's index
+    within its task): the queries are the last q_len positions of the task's
+    context (bottom-right alignment), so a task whose keys are a document's
+    prefix up to the end of a query chunk reproduces the document's causal
+    attention for that chunk.
+    """
+    qc = np.asarray(q_cu, dtype=np.int64)
+    kc = np.asarray(k_cu, dtype=np.int64)
+    rows = np.arange(int(qc[-1]), dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.arange(int(kc[-1]), dtype=np.int64) if keys is None else np.asarray(keys, dtype=np.int64)
+    tr = np.searchsorted(qc, rows, side="right") - 1
+    tk = np.searchsorted(kc, keys, side="right") - 1
+    m = tr[:, None] == tk[None, :]
+    if causal:
+        q_len = qc[tr + 1] - qc[tr]
+        k_len = kc[tr + 1] - kc[tr]
+        limit = kc[tr] + k_len - q_len + (rows - qc[tr]) + 1    # legal keys lie below this index
+        m &= keys[None, :] < limit[:, None]
+    return m
+
+
+def task_mask_fn(q_cu, k_cu, causal) -> MaskFn:
+    return lambda rows, keys: task_mask(q_cu, k_cu, causal, rows, keys)
+
+
 # ----------------------------------------------------------------------------- attention
 
 def _heads(q, k):
@@ -294,6 +327,15 @@ def varlen_fwd(q, k, v, cu_seqlens, causal, scale, rows=None):
 
 def varlen_bwd(q, k, v, dout, lse, delta, cu_seqlens, causal, scale, rows=None, keys=None):
     return attention_bwd(q, k, v, dout, lse, delta, varlen_mask_fn(cu_seqlens, causal), scale,
+                         rows=rows, keys=keys)
+
+
+def task_fwd(q, k, v, q_cu, k_cu, causal, scale, rows=None):
+    return attention_fwd(q, k, v, task_mask_fn(q_cu, k_cu, causal), scale, rows=rows)
+
+
+def task_bwd(q, k, v, dout, lse, delta, q_cu, k_cu, causal, scale, rows=None, keys=None):
+    return attention_bwd(q, k, v, dout, lse, delta, task_mask_fn(q_cu, k_cu, causal), scale,
                          rows=rows, keys=keys)
 
 

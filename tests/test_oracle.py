@@ -481,3 +481,93 @@ def test_varlen_config_lengths(orc):
     assert cfg.total == 262144 and len(cfg.seqlens) == 27
     assert min(cfg.seqlens) >= 128 and max(cfg.seqlens) <= 65536
     assert sum(n * (n + 1) // 2 for n in cfg.seqlens) == 3214974270
+
+
+# ----------------------------------------------------------------------------- core-attention tasks
+
+def _chunk_tasks(doc_lens, chunk):
+    """Documents split into query chunks of `chunk` rows; each task's keys are its
+    document's prefix up to the chunk's end (built here, independent of any library
+    scheduler).  Returns q_cu, k_cu and, per task key row, the document row it copies."""
+    q_cu, k_cu, src = [0], [0], []
+    start = 0
+    for n in doc_lens:
+        for c0 in range(0, n, chunk):
+            c1 = min(n, c0 + chunk)
+            q_cu.append(q_cu[-1] + (c1 - c0))
+            k_cu.append(k_cu[-1] + c1)
+            src.extend(range(start, start + c1))
+        start += n
+    return np.array(q_cu), np.array(k_cu), np.array(src, dtype=np.int64)
+
+
+def test_task_mask_reduces_to_varlen(orc):
+    cu = np.array([0, 3, 3, 10, 11, 30])
+    for causal in (True, False):
+        assert np.array_equal(orc.task_mask(cu, cu, causal), orc.varlen_mask(cu, causal))
+
+
+def test_task_prefix_chunks_reproduce_document_causal_attention(orc):
+    """Splitting each document into query chunks, each attending its document's
+    prefix (bottom-right causal), composes to plain causal attention per document:
+    O, LSE and dQ agree, and dK/dV summed back over the prefix copies agree."""
+    rng = np.random.default_rng(21)
+    doc_lens = [7, 13, 1, 20]
+    cu = np.concatenate([[0], np.cumsum(doc_lens)])
+    T = int(cu[-1])
+    hq, hkv, d, scale = 4, 2, 8, 0.3
+    q, k, v = _rand_qkv(rng, T, T, hq, hkv, d)
+    dout = rng.standard_normal((T, hq, d))
+    o_ref, lse_ref = orc.varlen_fwd(q, k, v, cu, True, scale)
+    D = orc.delta_rows(o_ref, dout)
+    dq_ref, dk_ref, dv_ref = orc.varlen_bwd(q, k, v, dout, lse_ref, D, cu, True, scale)
+    for chunk in (1, 4, 6, 64):
+        q_cu, k_cu, src = _chunk_tasks(doc_lens, chunk)
+        kt, vt = k[src], v[src]
+        o, lse = orc.task_fwd(q, kt, vt, q_cu, k_cu, True, scale)
+        assert np.allclose(o, o_ref, atol=1e-12) and np.allclose(lse, lse_ref, atol=1e-12)
+        dq, dkt, dvt = orc.task_bwd(q, kt, vt, dout, lse, D, q_cu, k_cu, True, scale)
+        assert np.allclose(dq, dq_ref, atol=1e-12)
+        dk = np.zeros_like(dk_ref)
+        dv = np.zeros_like(dv_ref)
+        np.add.at(dk, src, dkt)
+        np.add.at(dv, src, dvt)
+        assert np.allclose(dk, dk_ref, atol=1e-12) and np.allclose(dv, dv_ref, atol=1e-12)
+
+
+def test_task_noncausal_is_full_attention_per_task(orc):
+    rng = np.random.default_rng(22)
+    q_lens, k_lens = [3, 9, 1, 5], [11, 2, 7, 5]
+    q_cu = np.concatenate([[0], np.cumsum(q_lens)])
+    k_cu = np.concatenate([[0], np.cumsum(k_lens)])
+    q, k, v = _rand_qkv(rng, int(q_cu[-1]), int(k_cu[-1]), 4, 2, 8)
+    o, _ = orc.task_fwd(q, k, v, q_cu, k_cu, False, 0.2)
+    for t in range(len(q_lens)):
+        a, b, c, e = q_cu[t], q_cu[t + 1], k_cu[t], k_cu[t + 1]
+        assert np.allclose(o[a:b], _sdpa(q[a:b], k[c:e], v[c:e], False, 0.2), atol=1e-12)
+
+
+def test_task_context_shorter_than_queries_leaves_leading_rows_empty(orc):
+    """Bottom-right alignment with k_len < q_len: the first q_len - k_len rows see
+    no key (O = 0, LSE = -inf); row q_len - k_len + i sees keys 0..i."""
+    rng = np.random.default_rng(23)
+    q_cu, k_cu = np.array([0, 6]), np.array([0, 4])
+    q, k, v = _rand_qkv(rng, 6, 4, 2, 1, 8)
+    m = orc.task_mask(q_cu, k_cu, True)
+    assert not m[:2].any()
+    for i in range(4):
+        assert np.array_equal(m[2 + i], np.arange(4) <= i)
+    o, lse = orc.task_fwd(q, k, v, q_cu, k_cu, True, 0.5)
+    assert np.all(o[:2] == 0) and np.all(np.isneginf(lse[:, :2]))
+    assert np.allclose(o[5], _sdpa(q[5:6], k, v, False, 0.5)[0], atol=1e-12)
+
+
+def test_task_mask_matches_scalar_definition(orc):
+    q_cu, k_cu = [0, 2, 2, 7, 8], [0, 5, 9, 12, 20]
+    m = orc.task_mask(q_cu, k_cu, True)
+    for i in range(q_cu[-1]):
+        t = max(x for x in range(len(q_cu) - 1) if q_cu[x] <= i < q_cu[x + 1])
+        ql, kl = q_cu[t + 1] - q_cu[t], k_cu[t + 1] - k_cu[t]
+        for j in range(k_cu[-1]):
+            legal = k_cu[t] <= j < k_cu[t + 1] and (j - k_cu[t]) <= kl - ql + (i - q_cu[t])
+            assert m[i, j] == legal, (i, j)

@@ -35,6 +35,12 @@ MUTATIONS = [
      "lse = np.where(has, np.log(np.where(has, tot, 1.0)), NEG_INF)"),
     ("varlen_strict_causal", "m &= keys[None, :] <= rows[:, None]", "m &= keys[None, :] < rows[:, None]"),
     ("delta_transposed_heads", 'np.einsum("nhd,nhd->hn"', 'np.einsum("nhd,nhd->nh"'),
+    ("task_top_left_causal", "limit = kc[tr] + k_len - q_len + (rows - qc[tr]) + 1",
+     "limit = kc[tr] + (rows - qc[tr]) + 1"),
+    ("task_strict_causal", "limit = kc[tr] + k_len - q_len + (rows - qc[tr]) + 1",
+     "limit = kc[tr] + k_len - q_len + (rows - qc[tr])"),
+    ("task_keys_not_offset", "limit = kc[tr] + k_len - q_len + (rows - qc[tr]) + 1",
+     "limit = k_len - q_len + (rows - qc[tr]) + 1"),
 ]
 
 PIN_FUNCS = [(n, f) for n, f in vars(pins).items() if n.startswith("test_") and callable(f)]
