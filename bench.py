@@ -141,15 +141,33 @@ def merge_microbench(p, n_parts: int = 16, reps: int = 5):
 
 
 def bench_varlen(args, cfg):
-    """The varlen workload: packed token-causal shards, one forward and one
+    """The varlen workload (packed token-causal shards) or its core-attention task
+    form (the same documents cut into tasks that carry their prefix context,
+    gathered into one packed K/V before the timed region): one forward and one
     backward call per step (4d + 10d flops per useful pair and q-head)."""
+    import numpy as np
     import torch
+    from masked_long_context_amd import bdattn as B
     from masked_long_context_amd import workloads as wl
-    from masked_long_context_amd.rank_step import VarlenStep
+    from masked_long_context_amd.rank_step import TaskStep, VarlenStep
+    tasks = isinstance(cfg, wl.CadTaskConfig)
+    docs = cfg.docs if tasks else cfg
     print(f"# bench: generating inputs for {cfg.name}", file=sys.stderr, flush=True)
-    inp = wl.varlen_inputs(cfg, seed=0)
+    inp = wl.varlen_inputs(docs, seed=0)
     g = {k: v.cuda() for k, v in inp.items()}
-    step = VarlenStep(cfg.cu_seqlens, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
+    extra = {}
+    if tasks:
+        q_cu, k_cu, src = B.cad_split(docs.cu_seqlens, cfg.max_pairs)
+        idx = torch.from_numpy(wl.task_context_rows(k_cu, src)).cuda()
+        g["k"], g["v"] = g["k"].index_select(0, idx), g["v"].index_select(0, idx)
+        del idx
+        step = TaskStep(q_cu, k_cu, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
+        ql, kl = np.diff(q_cu), np.diff(k_cu)
+        extra = {"tasks": int(src.size), "max_pairs_per_task": cfg.max_pairs, "context_rows": int(k_cu[-1]),
+                 "task_q_len_min_med_max": [int(ql.min()), int(np.median(ql)), int(ql.max())],
+                 "task_k_len_max": int(kl.max())}
+    else:
+        step = VarlenStep(cfg.cu_seqlens, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
     timer = EventTimer()
     step.timer = timer
     pairs = step.useful_pairs
@@ -171,12 +189,13 @@ def bench_varlen(args, cfg):
     fwd_ms = tot["fwd"][0] / args.steps
     bwd_ms = tot["bwd"][0] / args.steps
     out = {
-        "metric": "varlen packed causal attention fwd+bwd useful-pair TFLOP/s", "value": round(tflops, 2),
+        "metric": ("core-attention task batch (prefix contexts) fwd+bwd useful-pair TFLOP/s" if tasks else
+                   "varlen packed causal attention fwd+bwd useful-pair TFLOP/s"), "value": round(tflops, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "shards": len(cfg.seqlens), "tokens": cfg.total, "h_q": cfg.h_q,
+        "config": {"workload": cfg.name, "shards": len(docs.seqlens), "tokens": docs.total, "h_q": cfg.h_q,
                    "h_kv": cfg.h_kv, "head_dim": cfg.head_dim, "useful_pairs_per_head": pairs,
-                   "flops_per_step": flops},
+                   "flops_per_step": flops, **extra},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels": {"fwd": {"ms": round(fwd_ms, 4),
                             "tflops": round(pairs * cfg.h_q * 4 * cfg.head_dim / (fwd_ms * 1e-3) / 1e12, 2)},
@@ -202,8 +221,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
-                    help="workload: 3 = the 256K rank share (default); 4 = varlen packed causal shards")
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6],
+                    help="workload: 3 = the 256K rank share (default); 4 = varlen packed causal shards; "
+                         "6 = workload 4's documents as core-attention tasks with prefix contexts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,7 +231,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} refused: this BDLM attention path runs on one GPU "
-              "(one CSBP rank's share); multi-GPU runs are not part of this build.", file=sys.stderr)
+              "(one CSBP rank's share); multi-GPU runs are not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -219,7 +239,7 @@ def main():
     from masked_long_context_amd.rank_step import BdlmRankStep
 
     cfg = wl.config(args.config)
-    if args.config == 4:
+    if args.config in (4, 6):
         bench_varlen(args, cfg)
         return
     p = cfg.problem

@@ -108,6 +108,40 @@ int bdattn_plan_create_varlen(const int32_t *cu_seqlens, int32_t n_seqs, int32_t
                               int32_t h_q, int32_t h_kv, int32_t head_dim, float softmax_scale,
                               bdattn_plan **out);
 
+/* Plan for core-attention tasks that carry their own key context ("Efficient
+ * Long-context Language Model Training by Core Attention Disaggregation",
+ * English abstract: core attention split into token-level tasks and rebatched
+ * into fused varlen batches).  q_cu and k_cu are HOST int32 arrays of
+ * n_tasks + 1 non-decreasing offsets starting at 0 (copied): task i owns query
+ * rows [q_cu[i], q_cu[i+1]) of the packed Q and key rows [k_cu[i], k_cu[i+1])
+ * of the packed K/V.  causal = 1 aligns the queries with the END of their
+ * context (bottom-right): query j of a task with q_len rows and k_len keys sees
+ * its keys 0 .. k_len - q_len + j (none when that is negative, so a task with
+ * k_len < q_len has leading rows with no key: O = 0, LSE = -inf).  causal = 0:
+ * every query sees all k_len keys.  Use it with the varlen compute calls,
+ * passing the packed task K/V as k and v (a task's context may repeat keys of
+ * another task; each copy gets its own dK/dV rows). */
+int bdattn_plan_create_tasks(const int32_t *q_cu, const int32_t *k_cu, int32_t n_tasks,
+                             int32_t causal, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                             float softmax_scale, bdattn_plan **out);
+
+/* Split packed causal documents into core-attention tasks of bounded work
+ * (same paper and passage: token-level tasks that a scheduler rebatches).
+ * cu_seqlens: HOST int32, n_docs + 1 non-decreasing offsets from 0.  Each
+ * document is cut into runs of consecutive rows, greedily from its first row,
+ * so that a run's causal pairs (row x of the document sees its x + 1 prefix
+ * keys) stay <= max_pairs_per_task; a single row above the bound forms its own
+ * task.  Task t gets the run as its queries and the document prefix up to the
+ * run's end as its key context, so its plan (causal = 1) reproduces causal
+ * attention of the document.  Writes at most cap tasks: q_cu and k_cu
+ * (cap + 1 entries, cumulative offsets into the packed task queries and task
+ * contexts) and kv_src (cap entries: packed row where the task's context
+ * starts, i.e. its document's first row).  Returns the number of tasks (call
+ * with cap = 0 to size the arrays) or a negative bdattn_status
+ * (BDATTN_EINVAL also when the summed context rows exceed 2^30). */
+int64_t bdattn_cad_split(const int32_t *cu_seqlens, int32_t n_docs, int64_t max_pairs_per_task,
+                         int32_t *q_cu, int32_t *k_cu, int32_t *kv_src, int64_t cap);
+
 void bdattn_plan_destroy(bdattn_plan *plan);
 
 /* Size (bytes) of the per-call workspace: the plan's tables, uploaded by each call. */
@@ -188,7 +222,9 @@ int bdattn_bwd_dq(const bdattn_plan *plan, const void *q, const void *k_clean, c
 /* dq (bf16) = dq_accum (fp32), n_elems elements. */
 int bdattn_dq_finalize(const float *dq_accum, void *dq, int64_t n_elems, void *stream);
 
-/* Varlen packed shards: the same kernels over a plan from bdattn_plan_create_varlen. */
+/* Varlen packed shards: the same kernels over a plan from bdattn_plan_create_varlen
+ * or bdattn_plan_create_tasks (k and v: [n_keys][h_kv][head_dim], n_keys =
+ * cu_seqlens[n_seqs] or k_cu[n_tasks]; dk and dv have the same shape). */
 int bdattn_varlen_fwd(const bdattn_plan *plan, const void *q, const void *k, const void *v, void *o,
                       int32_t o_dtype, float *lse, void *workspace, int64_t workspace_bytes,
                       void *stream);

@@ -43,6 +43,10 @@ _SIGS = {
     "bdattn_plan_create": (c_int32, [ctypes.POINTER(Problem), ctypes.POINTER(c_void_p)]),
     "bdattn_plan_create_varlen": (c_int32, [ctypes.POINTER(c_int32), c_int32, c_int32, c_int32, c_int32,
                                             c_int32, c_float, ctypes.POINTER(c_void_p)]),
+    "bdattn_plan_create_tasks": (c_int32, [ctypes.POINTER(c_int32), ctypes.POINTER(c_int32), c_int32, c_int32,
+                                           c_int32, c_int32, c_int32, c_float, ctypes.POINTER(c_void_p)]),
+    "bdattn_cad_split": (c_int64, [ctypes.POINTER(c_int32), c_int32, c_int64, ctypes.POINTER(c_int32),
+                                   ctypes.POINTER(c_int32), ctypes.POINTER(c_int32), c_int64]),
     "bdattn_plan_destroy": (None, [c_void_p]),
     "bdattn_plan_workspace_bytes": (c_int64, [c_void_p]),
     "bdattn_plan_useful_pairs": (c_int64, [c_void_p]),
@@ -138,6 +142,21 @@ class Plan:
         _check(lib().bdattn_plan_create_varlen(cu.ctypes.data_as(ctypes.POINTER(c_int32)), cu.size - 1,
                                                int(bool(causal)), h_q, h_kv, head_dim, softmax_scale,
                                                ctypes.byref(h)))
+        return cls(h)
+
+    @classmethod
+    def tasks(cls, q_cu, k_cu, causal, h_q, h_kv, head_dim, softmax_scale=0.0):
+        """Core-attention tasks: task i owns query rows [q_cu[i], q_cu[i+1]) and key
+        context [k_cu[i], k_cu[i+1]); causal masks align queries with the context end."""
+        qc = np.ascontiguousarray(np.asarray(q_cu, dtype=np.int32))
+        kc = np.ascontiguousarray(np.asarray(k_cu, dtype=np.int32))
+        if qc.size != kc.size:
+            raise BdattnError(EINVAL, "q_cu and k_cu must have the same length")
+        h = c_void_p()
+        p32 = ctypes.POINTER(c_int32)
+        _check(lib().bdattn_plan_create_tasks(qc.ctypes.data_as(p32), kc.ctypes.data_as(p32), qc.size - 1,
+                                              int(bool(causal)), h_q, h_kv, head_dim, softmax_scale,
+                                              ctypes.byref(h)))
         return cls(h)
 
     @property
@@ -236,6 +255,29 @@ def bdattn_varlen_bwd(plan: Plan, q, k, v, dout, lse, delta, dq_accum, dk, dv, w
 
 def bdattn_dq_finalize(dq_accum, dq, stream=None):
     _check(lib().bdattn_dq_finalize(_ptr(dq_accum), _ptr(dq), dq_accum.numel(), _stream(stream)))
+
+
+def cad_split(cu_seqlens, max_pairs_per_task: int):
+    """Split packed causal documents into bounded-work tasks with prefix context.
+
+    Returns (q_cu, k_cu, kv_src) as int32 arrays: task t's queries are packed rows
+    [q_cu[t], q_cu[t+1]) in document order, its context has k_cu[t+1] - k_cu[t]
+    rows starting at packed row kv_src[t]."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    p32 = ctypes.POINTER(c_int32)
+    n = lib().bdattn_cad_split(cu.ctypes.data_as(p32), cu.size - 1, int(max_pairs_per_task), None, None, None, 0)
+    if n < 0:
+        _check(int(n))
+    q_cu = np.zeros(n + 1, np.int32)
+    k_cu = np.zeros(n + 1, np.int32)
+    kv_src = np.zeros(max(n, 1), np.int32)
+    if n > 0:
+        got = lib().bdattn_cad_split(cu.ctypes.data_as(p32), cu.size - 1, int(max_pairs_per_task),
+                                     q_cu.ctypes.data_as(p32), k_cu.ctypes.data_as(p32),
+                                     kv_src.ctypes.data_as(p32), n)
+        if got != n:
+            raise BdattnError(EINVAL, f"bdattn_cad_split returned {got}, expected {n}")
+    return q_cu, k_cu, kv_src[:n]
 
 
 def last_error() -> str:

@@ -224,6 +224,42 @@ int bdattn_plan_create(const bdattn_problem *pr, bdattn_plan **out) {
   }
 }
 
+int bdattn_plan_create_tasks(const int32_t *q_cu, const int32_t *k_cu, int32_t n_tasks, int32_t causal, int32_t h_q,
+                             int32_t h_kv, int32_t head_dim, float scale, bdattn_plan **out) {
+  if (!out) return fail(BDATTN_EINVAL, "out is NULL");
+  try {
+    bdattn_plan *pl = new bdattn_plan;
+    std::string e = bdattn::build_tasks(pl->p, q_cu, k_cu, n_tasks, causal != 0, h_q, h_kv, head_dim, scale);
+    if (!e.empty()) {
+      delete pl;
+      return fail_build(e);
+    }
+    *out = pl;
+    return BDATTN_OK;
+  } catch (const std::bad_alloc &) {
+    return fail(BDATTN_EINVAL, "out of host memory building the plan");
+  } catch (const std::exception &x) {
+    return fail(BDATTN_EINVAL, x.what());
+  }
+}
+
+int64_t bdattn_cad_split(const int32_t *cu, int32_t n_docs, int64_t max_pairs, int32_t *q_cu, int32_t *k_cu,
+                         int32_t *kv_src, int64_t cap) {
+  if (!cu) return fail(BDATTN_EINVAL, "cu_seqlens is NULL");
+  if (n_docs < 0) return fail(BDATTN_EINVAL, "n_docs must be >= 0");
+  if (max_pairs < 1) return fail(BDATTN_EINVAL, "max_pairs_per_task must be >= 1");
+  if (cap < 0) return fail(BDATTN_EINVAL, "cap must be >= 0");
+  if (cap > 0 && (!q_cu || !k_cu || !kv_src)) return fail(BDATTN_EINVAL, "output arrays are NULL");
+  if (cu[0] != 0) return fail(BDATTN_EINVAL, "cu_seqlens[0] must be 0");
+  for (int32_t s = 0; s < n_docs; ++s)
+    if (cu[s + 1] < cu[s]) return fail(BDATTN_EINVAL, "cu_seqlens must be non-decreasing");
+  int64_t total_ctx = 0;
+  const int64_t n = bdattn::cad_split(cu, n_docs, max_pairs, nullptr, nullptr, nullptr, 0, &total_ctx);
+  if (total_ctx > INT32_MAX / 2) return fail(BDATTN_EINVAL, "the tasks' key contexts exceed 2^30 rows");
+  if (cap > 0) bdattn::cad_split(cu, n_docs, max_pairs, q_cu, k_cu, kv_src, cap, nullptr);
+  return n;
+}
+
 int bdattn_plan_create_varlen(const int32_t *cu, int32_t n_seqs, int32_t causal, int32_t h_q, int32_t h_kv,
                               int32_t head_dim, float scale, bdattn_plan **out) {
   if (!out) return fail(BDATTN_EINVAL, "out is NULL");

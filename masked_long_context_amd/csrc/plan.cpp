@@ -224,6 +224,70 @@ std::string build_bdlm(Plan &p, int64_t L, int32_t B, int64_t q_off, int64_t q_l
   return "";
 }
 
+std::string build_tasks(Plan &p, const int32_t *q_cu, const int32_t *k_cu, int32_t n, bool causal, int32_t h_q,
+                        int32_t h_kv, int32_t d, float scale) {
+  if (!q_cu || !k_cu) return "q_cu / k_cu is NULL";
+  if (n < 0) return "n_tasks must be >= 0";
+  if (q_cu[0] != 0 || k_cu[0] != 0) return "q_cu[0] and k_cu[0] must be 0";
+  for (int32_t t = 0; t < n; ++t)
+    if (q_cu[t + 1] < q_cu[t] || k_cu[t + 1] < k_cu[t]) return "q_cu and k_cu must be non-decreasing";
+  std::string e = check_heads(h_q, h_kv, d);
+  if (!e.empty()) return e;
+  const int64_t Tq = q_cu[n], Tk = k_cu[n];
+  if (Tq > INT32_MAX / 2 || Tk > INT32_MAX / 2) return "problem too large";
+  p.kind = 1;
+  p.h_q = h_q; p.h_kv = h_kv; p.d = d;
+  p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  p.n_q = Tq;
+  p.n_seg[0] = Tk;
+  p.n_seg[1] = 0;
+  p.rows.assign(Tq * 4, 0);
+  std::vector<Region> regions;
+  for (int32_t t = 0; t < n; ++t) {
+    const int64_t q_len = q_cu[t + 1] - q_cu[t], k_len = k_cu[t + 1] - k_cu[t];
+    for (int64_t i = 0; i < q_len; ++i) {
+      // bottom-right alignment: the queries are the last q_len positions of the context
+      const int64_t seen = causal ? std::min(k_len, std::max<int64_t>(0, k_len - q_len + i + 1)) : k_len;
+      const int64_t r = q_cu[t] + i;
+      p.rows[r * 4 + 0] = k_cu[t];
+      p.rows[r * 4 + 1] = (int32_t)(k_cu[t] + seen);
+    }
+    if (q_len > 0) regions.push_back(Region{q_cu[t], q_cu[t + 1]});
+  }
+  tile_regions(p, regions);
+  finish(p);
+  return "";
+}
+
+int64_t cad_split(const int32_t *cu, int32_t n_docs, int64_t max_pairs, int32_t *q_cu, int32_t *k_cu,
+                  int32_t *kv_src, int64_t cap, int64_t *total_ctx) {
+  int64_t t = 0;
+  if (cap > 0) {
+    q_cu[0] = 0;
+    k_cu[0] = 0;
+  }
+  int64_t qa = 0, ka = 0;
+  for (int32_t s = 0; s < n_docs; ++s) {
+    const int64_t start = cu[s], L = cu[s + 1] - cu[s];
+    for (int64_t b = 0; b < L;) {
+      // rows b .. e-1 of the document; row x sees the x + 1 keys of its prefix
+      int64_t e = b + 1, pairs = b + 1;
+      while (e < L && pairs + (e + 1) <= max_pairs) pairs += ++e;
+      qa += e - b;
+      ka += e;
+      if (t < cap) {
+        q_cu[t + 1] = (int32_t)qa;
+        k_cu[t + 1] = (int32_t)ka;
+        kv_src[t] = (int32_t)start;
+      }
+      ++t;
+      b = e;
+    }
+  }
+  if (total_ctx) *total_ctx = ka;
+  return t;
+}
+
 std::string build_varlen(Plan &p, const int32_t *cu, int32_t n_seqs, bool causal, int32_t h_q,
                          int32_t h_kv, int32_t d, float scale) {
   if (!cu) return "cu_seqlens is NULL";

@@ -56,6 +56,13 @@ std::string build_bdlm(Plan &p, int64_t clean_len, int32_t B, int64_t q_off, int
                        bool local, int32_t h_q, int32_t h_kv, int32_t d, float scale);
 std::string build_varlen(Plan &p, const int32_t *cu, int32_t n_seqs, bool causal, int32_t h_q,
                          int32_t h_kv, int32_t d, float scale);
+std::string build_tasks(Plan &p, const int32_t *q_cu, const int32_t *k_cu, int32_t n, bool causal, int32_t h_q,
+                        int32_t h_kv, int32_t d, float scale);
+// Core-attention tasks with prefix context from packed documents; returns the task
+// count and the summed context rows (writes at most cap tasks: q_cu / k_cu hold
+// cap + 1 entries, kv_src cap).
+int64_t cad_split(const int32_t *cu, int32_t n_docs, int64_t max_pairs, int32_t *q_cu, int32_t *k_cu,
+                  int32_t *kv_src, int64_t cap, int64_t *total_ctx);
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 

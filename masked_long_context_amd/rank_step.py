@@ -103,17 +103,18 @@ class BdlmRankStep:
 class VarlenStep:
     """Forward + backward of packed independent shards (one call each)."""
 
-    def __init__(self, cu_seqlens, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0):
-        self.plan = B.Plan.varlen(cu_seqlens, causal, h_q, h_kv, head_dim, softmax_scale)
-        T = int(cu_seqlens[-1])
-        self.T, self.h_q, self.h_kv, self.d = T, h_q, h_kv, head_dim
+    def __init__(self, cu_seqlens, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0, plan=None):
+        self.plan = plan if plan is not None else B.Plan.varlen(cu_seqlens, causal, h_q, h_kv, head_dim,
+                                                                softmax_scale)
+        T, n_keys = self.plan.n_q, self.plan.n_kv(0)
+        self.T, self.n_keys, self.h_q, self.h_kv, self.d = T, n_keys, h_q, h_kv, head_dim
         self.ws = B.workspace(self.plan.workspace_bytes, device)
         self.o = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((h_q, T), dtype=torch.float32, device=device)
         self.delta = torch.empty((h_q, T), dtype=torch.float32, device=device)
         self.dq_acc = torch.empty((T, h_q, head_dim), dtype=torch.float32, device=device)
         self.dq = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
-        self.dk = torch.empty((T, h_kv, head_dim), dtype=torch.bfloat16, device=device)
+        self.dk = torch.empty((n_keys, h_kv, head_dim), dtype=torch.bfloat16, device=device)
         self.dv = torch.empty_like(self.dk)
         self.timer = None      # optional callable(tag) -> context manager around each library call
 
@@ -143,3 +144,13 @@ class VarlenStep:
     def step(self, q, k, v, dout):
         self.forward(q, k, v)
         return self.backward(q, k, v, dout)
+
+
+class TaskStep(VarlenStep):
+    """Forward + backward of a fused batch of core-attention tasks, each with its own
+    key context (packed task queries [q_cu[-1], h_q, d], packed contexts
+    [k_cu[-1], h_kv, d]); dk/dv hold one gradient per context row."""
+
+    def __init__(self, q_cu, k_cu, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0):
+        plan = B.Plan.tasks(q_cu, k_cu, causal, h_q, h_kv, head_dim, softmax_scale)
+        super().__init__(None, causal, h_q, h_kv, head_dim, device, softmax_scale, plan=plan)

@@ -17,7 +17,7 @@ Sources (web pages on block-diffusion training):
     Disaggregation", English abstract: core attention over fused batches of
     token-level shards of arbitrary length.
 
-Readings taken where the pages are silent (all listed in the design doc):
+Readings taken where the pages are silent:
   * ownership is a zigzag: rank r of R owns the block pairs (k, N_b-1-k) for
     k in [r*n, (r+1)*n) with n = N_b / (2R); rows list the early range
     ascending, then the late range ascending;
@@ -120,6 +120,47 @@ class VarlenConfig:
         return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.head_dim)
 
 
+@dataclasses.dataclass(frozen=True)
+class CadTaskConfig:
+    """Packed causal documents cut into core-attention tasks with prefix context.
+
+    The library's task splitter cuts every document of ``docs`` into runs of rows
+    whose causal pairs stay within ``max_pairs`` ("Efficient Long-context Language
+    Model Training by Core Attention Disaggregation", English abstract: token-level
+    tasks rebatched to equalize compute); each task carries its document's prefix
+    up to the run's end as key context, gathered into one packed K/V."""
+    name: str
+    docs: VarlenConfig
+    max_pairs: int
+    description: str
+
+    @property
+    def h_q(self) -> int:
+        return self.docs.h_q
+
+    @property
+    def h_kv(self) -> int:
+        return self.docs.h_kv
+
+    @property
+    def head_dim(self) -> int:
+        return self.docs.head_dim
+
+    @property
+    def scale(self) -> float:
+        return self.docs.scale
+
+
+def task_context_rows(k_cu, kv_src) -> np.ndarray:
+    """Packed document row of every context row of every task (int64): the gather index."""
+    k_cu = np.asarray(k_cu, dtype=np.int64)
+    src = np.asarray(kv_src, dtype=np.int64)
+    lens = np.diff(k_cu)
+    if lens.size == 0:
+        return np.zeros(0, np.int64)
+    return np.repeat(src - k_cu[:-1], lens) + np.arange(int(k_cu[-1]), dtype=np.int64)
+
+
 def zigzag_owned_blocks(n_blocks: int, ranks: int, rank: int) -> np.ndarray:
     """Corrupted blocks owned by ``rank``: early range then mirrored late range."""
     if n_blocks % (2 * ranks) != 0:
@@ -167,7 +208,8 @@ def _bdlm_config(name, L, B, R, rank, hq, hkv, d, scale, n_shards, local_shard, 
 
 
 def config(idx: int):
-    """Workloads 1..5 (1: tiny, 2: 4K GQA, 3: 256K/16 rank share, 4: varlen, 5: 1M/8 rank share)."""
+    """Workloads 1..6 (1: tiny, 2: 4K GQA, 3: 256K/16 rank share, 4: varlen, 5: 1M/8 rank share,
+    6: workload 4 as core-attention tasks with prefix context)."""
     if idx == 1:
         return _bdlm_config("tiny_L256_B32_h1_d64", 256, 32, 1, 0, 1, 1, 64, 1.0, 1, 0,
                             "L=256, B=32, 1/1 heads, d=64, unsharded, all 8 blocks")
@@ -185,6 +227,10 @@ def config(idx: int):
     if idx == 5:
         return _bdlm_config("csbp_1M_r4of8_B16_h32x8_d128", 1048576, 16, 8, 4, 32, 8, 128, 1.0,
                             8, 4, "1M clean context split 8 ways, rank 4, B=16, 32/8 heads, d=128")
+    if idx == 6:
+        return CadTaskConfig(name="cad_tasks_262144_max2p26_h32x8_d128", docs=config(4), max_pairs=1 << 26,
+                             description="workload 4's documents as core-attention tasks of at most 2^26 "
+                                         "causal pairs, each with its prefix context")
     raise ValueError(idx)
 
 
@@ -243,6 +289,16 @@ def varlen_inputs(cfg: VarlenConfig, seed: int = 0, names: Optional[Sequence[str
         sc = 1.0 if nm == "dout" else cfg.input_scale
         out[nm] = _randn_bf16(shapes[nm], seed, TENSOR_INDEX[nm], sc)
     return out
+
+
+def task_inputs(n_q: int, n_keys: int, h_q: int, h_kv: int, head_dim: int, seed: int = 0,
+                input_scale: float = 1.0) -> Dict:
+    """Seeded bf16 CPU tensors for a fused batch of core-attention tasks with their
+    own contexts: q, dout [n_q, h_q, d]; k, v [n_keys, h_kv, d]."""
+    shapes = {"q": (n_q, h_q, head_dim), "dout": (n_q, h_q, head_dim),
+              "k": (n_keys, h_kv, head_dim), "v": (n_keys, h_kv, head_dim)}
+    return {nm: _randn_bf16(shp, seed, TENSOR_INDEX[nm], 1.0 if nm == "dout" else input_scale)
+            for nm, shp in shapes.items()}
 
 
 def merge_partials_inputs(n_parts: int, n_rows: int, h: int, d: int, seed: int = 0,

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from masked_long_context_amd import workloads as wl
-from masked_long_context_amd.rank_step import BdlmRankStep, VarlenStep
+from masked_long_context_amd.rank_step import BdlmRankStep, TaskStep, VarlenStep
 
 # bf16 outputs O, dQ, dK, dV: max abs error and relative L2 error; fp32 LSE: max abs error
 TOL_MAX_ABS = 2e-2
@@ -120,4 +120,22 @@ def oracle_varlen(cu, causal, scale, inp) -> dict:
     o, lse = oracle.varlen_fwd(q, k, v, cu, causal, scale)
     D = oracle.delta_rows(o, do)
     dq, dk, dv = oracle.varlen_bwd(q, k, v, do, lse, D, cu, causal, scale)
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+def run_gpu_tasks(q_cu, k_cu, causal, h_q, h_kv, d, inp, poison=True) -> dict:
+    g = {k: v.to("cuda") for k, v in inp.items()}
+    step = TaskStep(q_cu, k_cu, causal, h_q, h_kv, d)
+    if poison:
+        poison_(step.o, step.lse, step.delta, step.dq_acc, step.dq, step.dk, step.dv)
+    step.step(g["q"], g["k"], g["v"], g["dout"])
+    torch.cuda.synchronize()
+    return dict(o=step.o, lse=step.lse, dq=step.dq, dk=step.dk, dv=step.dv, step=step)
+
+
+def oracle_tasks(q_cu, k_cu, causal, scale, inp) -> dict:
+    q, k, v, do = (to64(inp[n]) for n in ("q", "k", "v", "dout"))
+    o, lse = oracle.task_fwd(q, k, v, q_cu, k_cu, causal, scale)
+    D = oracle.delta_rows(o, do)
+    dq, dk, dv = oracle.task_bwd(q, k, v, do, lse, D, q_cu, k_cu, causal, scale)
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)

@@ -22,7 +22,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["bdattn_fwd", "bdattn_bwd", "bdattn_lse_merge", "bdattn_varlen_fwd", "bdattn_varlen_bwd",
-              "bdattn_plan_create", "bdattn_plan_create_varlen", "bdattn_bwd_prepare", "bdattn_dq_finalize"]:
+              "bdattn_plan_create", "bdattn_plan_create_varlen", "bdattn_bwd_prepare", "bdattn_dq_finalize",
+              "bdattn_plan_create_tasks", "bdattn_cad_split"]:
         assert n in names
 
 
@@ -68,6 +69,44 @@ def test_varlen_plan_rejects():
     assert _status(lambda: B.Plan.varlen([1, 5], True, 4, 2, 128)) == B.EINVAL
     assert _status(lambda: B.Plan.varlen([0, 5, 3], True, 4, 2, 128)) == B.EINVAL
     assert _status(lambda: B.Plan.varlen([0, 5], True, 4, 2, 80)) == B.EUNSUPPORTED
+
+
+def test_task_plan_rejects():
+    assert _status(lambda: B.Plan.tasks([1, 5], [0, 5], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, 5], [2, 5], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, 5, 3], [0, 5, 9], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, 5, 9], [0, 5, 4], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, 5], [0, 5, 7], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, 5], [0, 5], True, 3, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, 5], [0, 5], True, 4, 2, 96)) == B.EUNSUPPORTED
+    big = 1 << 30
+    assert _status(lambda: B.Plan.tasks([0, 1], [0, big], True, 4, 2, 128)) == B.EINVAL
+
+
+def test_task_plan_null_and_negative_counts():
+    lib = B.lib()
+    h = ctypes.c_void_p()
+    cu = (ctypes.c_int32 * 2)(0, 4)
+    assert lib.bdattn_plan_create_tasks(None, cu, 1, 1, 4, 2, 128, 0.0, ctypes.byref(h)) == B.EINVAL
+    assert lib.bdattn_plan_create_tasks(cu, None, 1, 1, 4, 2, 128, 0.0, ctypes.byref(h)) == B.EINVAL
+    assert lib.bdattn_plan_create_tasks(cu, cu, -1, 1, 4, 2, 128, 0.0, ctypes.byref(h)) == B.EINVAL
+    assert lib.bdattn_plan_create_tasks(cu, cu, 1, 1, 4, 2, 128, 0.0, None) == B.EINVAL
+
+
+def test_cad_split_rejects():
+    lib = B.lib()
+    cu = (ctypes.c_int32 * 3)(0, 4, 9)
+    assert lib.bdattn_cad_split(None, 2, 10, None, None, None, 0) == B.EINVAL
+    assert lib.bdattn_cad_split(cu, -1, 10, None, None, None, 0) == B.EINVAL
+    assert lib.bdattn_cad_split(cu, 2, 0, None, None, None, 0) == B.EINVAL
+    assert lib.bdattn_cad_split(cu, 2, 10, None, None, None, -1) == B.EINVAL
+    assert lib.bdattn_cad_split(cu, 2, 10, None, None, None, 4) == B.EINVAL   # cap > 0, NULL outputs
+    assert _status(lambda: B.cad_split([1, 4], 10)) == B.EINVAL
+    assert _status(lambda: B.cad_split([0, 4, 2], 10)) == B.EINVAL
+    # one 2^16-row document cut into single rows: contexts sum to ~2^31 rows
+    assert _status(lambda: B.cad_split([0, 1 << 16], 1)) == B.EINVAL
+    # counting call (cap = 0) writes nothing and returns the task count
+    assert lib.bdattn_cad_split(cu, 2, 10, None, None, None, 0) == 3
 
 
 class FakeTensor:

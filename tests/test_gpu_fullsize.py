@@ -19,7 +19,8 @@ import torch
 
 import oracle
 from masked_long_context_amd import workloads as wl
-from masked_long_context_amd.rank_step import BdlmRankStep, VarlenStep
+from masked_long_context_amd import bdattn as B
+from masked_long_context_amd.rank_step import BdlmRankStep, TaskStep, VarlenStep
 from gpu_util import TOL_REL_L2, check_close, check_lse, need_gpu, poison_, to64
 
 pytestmark = pytest.mark.gpu
@@ -176,3 +177,63 @@ def test_varlen_262k_fullsize():
     _, dk_r, dv_r = oracle.varlen_bwd(q, k, v, do, lse_a, D, cu, True, cfg.scale, rows=arows, keys=keys)
     check_close("dk[keys]", dk[keys, :1], dk_r)
     check_close("dv[keys]", dv[keys, :1], dv_r)
+
+
+def test_cad_tasks_262k_fullsize():
+    """Workload 4's documents as core-attention tasks with gathered prefix contexts, at full size."""
+    need_gpu()
+    cfg = wl.config(6)
+    docs = cfg.docs
+    cu = docs.cu_seqlens
+    q_cu, k_cu, src = B.cad_split(cu, cfg.max_pairs)
+    rows = wl.task_context_rows(k_cu, src)
+    log(f"{cfg.name}: {len(src)} tasks, {len(rows)} context rows; generating inputs")
+    inp = wl.varlen_inputs(docs, seed=0)
+    g = {k: v.cuda() for k, v in inp.items()}
+    idx = torch.from_numpy(rows).cuda()
+    kt, vt = g["k"].index_select(0, idx), g["v"].index_select(0, idx)
+    step = TaskStep(q_cu, k_cu, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
+    poison_(step.o, step.lse, step.dq, step.dk, step.dv)
+    log(f"{cfg.name}: GPU step")
+    step.step(g["q"], kt, vt, g["dout"])
+    torch.cuda.synchronize()
+    G = cfg.h_q // cfg.h_kv
+    # every task is an independent attention problem over its own context copy
+    for t in range(len(src)):
+        a, b, c, e = int(q_cu[t]), int(q_cu[t + 1]), int(k_cu[t]), int(k_cu[t + 1])
+        check_sum_identities(step.dk[c:e], step.dv[c:e], g["dout"][a:b], G, f"task {t} (q {b - a}, ctx {e - c})")
+    o, lse, dq, dk, dv = (t.cpu() for t in (step.o, step.lse, step.dq, step.dk, step.dv))
+    del g, kt, vt, idx, step
+
+    # sampled rows: a task's queries are its document's rows, so O, LSE, dQ are the documents'
+    q = _f64(inp["q"][:, :G])
+    do = _f64(inp["dout"][:, :G])
+    k, v = _f64(inp["k"][:, :1]), _f64(inp["v"][:, :1])
+    rng = np.random.default_rng(6)
+    rs = np.sort(rng.choice(docs.total, 48, replace=False))
+    log(f"{cfg.name}: oracle on {len(rs)} sampled rows")
+    o_r, lse_r = oracle.varlen_fwd(q, k, v, cu, True, cfg.scale, rows=rs)
+    D = oracle.delta_rows(o_r, do[rs])
+    dq_r, _, _ = oracle.varlen_bwd(q, k, v, do, lse_r, D, cu, True, cfg.scale, rows=rs)
+    check_lse("lse[rows]", lse[:G, rs], lse_r)
+    check_close("o[rows]", o[rs, :G], o_r)
+    check_close("dq[rows]", dq[rs, :G], dq_r)
+
+    # dK/dV copies of two tasks, each against the oracle of that task alone: every key of the
+    # smallest task, and the last 48 context keys of the task with the longest context
+    ql, kl = np.diff(q_cu), np.diff(k_cu)
+    for t, nk in ((int(np.argmin(ql * kl)), None), (int(np.argmax(kl)), 48)):
+        a, b, c, e = int(q_cu[t]), int(q_cu[t + 1]), int(k_cu[t]), int(k_cu[t + 1])
+        tq, tdo = q[a:b], do[a:b]
+        tk, tv = k[rows[c:e]], v[rows[c:e]]
+        one_q, one_k = [0, b - a], [0, e - c]
+        keys = np.arange(e - c) if nk is None else np.arange(e - c - nk, e - c)
+        arows = np.nonzero(oracle.task_mask(one_q, one_k, True, keys=keys).any(axis=1))[0]
+        log(f"{cfg.name}: task {t} (q {b - a}, ctx {e - c}): oracle dK/dV on {len(keys)} keys "
+            f"({len(arows)} attending rows)")
+        o_a, lse_a = oracle.task_fwd(tq, tk, tv, one_q, one_k, True, cfg.scale, rows=arows)
+        D = oracle.delta_rows(o_a, tdo[arows])
+        _, dk_r, dv_r = oracle.task_bwd(tq, tk, tv, tdo, lse_a, D, one_q, one_k, True, cfg.scale,
+                                        rows=arows, keys=keys)
+        check_close(f"dk[task {t}]", dk[c + keys, :1], dk_r)
+        check_close(f"dv[task {t}]", dv[c + keys, :1], dv_r)

@@ -8,8 +8,9 @@ import torch
 import oracle
 from masked_long_context_amd import bdattn as B
 from masked_long_context_amd import workloads as wl
-from gpu_util import (check_close, check_lse, compare_bdlm, need_gpu, oracle_bdlm_full, oracle_varlen,
-                      poison_, run_gpu_bdlm, run_gpu_varlen, to64)
+from gpu_util import (TOL_MAX_ABS, TOL_REL_L2, check_close, check_lse, compare_bdlm, need_gpu,
+                      oracle_bdlm_full, oracle_tasks, oracle_varlen, poison_, run_gpu_bdlm, run_gpu_tasks,
+                      run_gpu_varlen, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +88,57 @@ def test_varlen_small(lens, causal, hq, hkv, d):
     check_lse("lse", got["lse"], want["lse"])
     for k in ("o", "dq", "dk", "dv"):
         check_close(k, got[k], want[k])
+
+
+@pytest.mark.parametrize("q_lens,k_lens,causal,hq,hkv,d", [
+    ([3, 130, 64, 1, 257], [3, 200, 64, 900, 257], True, 4, 2, 128),   # prefix contexts, k_len >= q_len
+    ([70, 5, 300], [10, 0, 129], True, 2, 1, 64),                       # leading rows without keys; no keys
+    ([0, 40, 0, 65], [12, 40, 0, 300], True, 4, 4, 64),                 # tasks without queries or keys
+    ([7, 129, 128, 1], [300, 33, 128, 64], False, 2, 1, 128),
+])
+def test_tasks_small(q_lens, k_lens, causal, hq, hkv, d):
+    """Core-attention tasks with their own contexts (bottom-right causal); dO halved as for varlen."""
+    q_cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    k_cu = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+    inp = wl.task_inputs(int(q_cu[-1]), int(k_cu[-1]), hq, hkv, d, seed=3)
+    inp["dout"] = (inp["dout"].float() * 0.5).to(torch.bfloat16)
+    print(f"tasks q={q_lens} k={k_lens} causal={causal} heads {hq}/{hkv} d={d}", flush=True)
+    got = run_gpu_tasks(q_cu, k_cu, causal, hq, hkv, d, inp)
+    want = oracle_tasks(q_cu, k_cu, causal, 1.0 / np.sqrt(d), inp)
+    check_lse("lse", got["lse"], want["lse"])
+    for k in ("o", "dq", "dk", "dv"):
+        check_close(k, got[k], want[k])
+
+
+def test_cad_tasks_reproduce_document_attention():
+    """Documents cut by the task splitter, contexts gathered per task: O, LSE and dQ equal the
+    documents' causal attention; each context copy's dK/dV equals its task's, and the copies
+    summed at their document rows give the documents' dK/dV."""
+    lens, max_pairs, hq, hkv, d = [300, 1, 700, 129, 64], 20000, 4, 2, 128
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q_cu, k_cu, src = B.cad_split(cu, max_pairs)
+    rows = wl.task_context_rows(k_cu, src)
+    cfg = wl.VarlenConfig("docs", tuple(lens), hq, hkv, d, True, 1.0, "")
+    docs = wl.varlen_inputs(cfg, seed=5)
+    docs["dout"] = (docs["dout"].float() * 0.5).to(torch.bfloat16)
+    tasks = dict(q=docs["q"], dout=docs["dout"], k=docs["k"][rows], v=docs["v"][rows])
+    print(f"{len(src)} tasks, {len(rows)} context rows", flush=True)
+    got = run_gpu_tasks(q_cu, k_cu, True, hq, hkv, d, tasks)
+    want_d = oracle_varlen(cu, True, cfg.scale, docs)
+    want_t = oracle_tasks(q_cu, k_cu, True, cfg.scale, tasks)
+    check_lse("lse vs documents", got["lse"], want_d["lse"])
+    for k in ("o", "dq"):
+        check_close(f"{k} vs documents", got[k], want_d[k])
+    for k in ("dk", "dv"):
+        check_close(f"{k} copies vs tasks", got[k], want_t[k])
+    # a document key has one copy per task of its document that reaches it; each copy is within
+    # the bf16 bound, so their sum is within that bound times the number of copies
+    copies = np.bincount(rows, minlength=cu[-1])
+    for k in ("dk", "dv"):
+        summed = np.zeros(want_d[k].shape)
+        np.add.at(summed, rows, to64(got[k]))
+        check_close(f"{k} copies summed vs documents", summed, want_d[k],
+                    max_abs=TOL_MAX_ABS * int(copies.max()), rel=TOL_REL_L2)
 
 
 @pytest.mark.parametrize("S,N,H,d,pdt,odt", [(5, 1000, 3, 128, torch.float32, torch.bfloat16),

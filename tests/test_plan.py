@@ -157,3 +157,82 @@ def test_useful_pairs_of_workloads(idx, expected):
 def test_varlen_workload_pairs():
     cfg = wl.config(4)
     assert B.Plan.varlen(cfg.cu_seqlens, True, 32, 8, 128).useful_pairs == 3214974270
+
+
+@pytest.mark.parametrize("q_lens,k_lens,causal", [
+    ([3, 130, 64, 1, 257], [3, 200, 64, 900, 257], True),      # prefix contexts, k_len >= q_len
+    ([70, 5, 300], [10, 0, 129], True),                         # k_len < q_len: leading rows see nothing
+    ([0, 40, 0, 65], [12, 40, 0, 300], True),                   # empty tasks on either side
+    ([7, 129, 128, 1], [300, 5, 128, 64], False),
+])
+def test_task_plans_match_mask(q_lens, k_lens, causal):
+    q_cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    k_cu = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+    plan = B.Plan.tasks(q_cu, k_cu, causal, 4, 2, 128)
+    m = oracle.task_mask(q_cu, k_cu, causal)
+    assert plan.n_q == int(q_cu[-1]) and plan.n_kv(0) == int(k_cu[-1]) and plan.n_kv(1) == 0
+    _check_plan(plan, m, int(k_cu[-1]), 0)
+
+
+def test_random_task_plans_match_mask():
+    rng = np.random.default_rng(1)
+    for _ in range(30):
+        n = int(rng.integers(1, 6))
+        q_lens = rng.integers(0, 300, n)
+        k_lens = np.where(rng.random(n) < 0.7, q_lens + rng.integers(0, 300, n), rng.integers(0, 300, n))
+        causal = bool(rng.integers(0, 2))
+        q_cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        k_cu = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
+        plan = B.Plan.tasks(q_cu, k_cu, causal, 2, 1, 64)
+        _check_plan(plan, oracle.task_mask(q_cu, k_cu, causal), int(k_cu[-1]), 0)
+
+
+def _check_cad_split(cu, max_pairs):
+    cu = np.asarray(cu, np.int64)
+    q_cu, k_cu, src = B.cad_split(cu, max_pairs)
+    n = src.size
+    assert q_cu.size == n + 1 and k_cu.size == n + 1 and q_cu[0] == 0 and k_cu[0] == 0
+    # the task queries are the packed document rows, in order, each exactly once
+    assert q_cu[-1] == cu[-1] and np.all(np.diff(q_cu) >= 1)
+    doc = np.searchsorted(cu, q_cu[:-1], side="right") - 1
+    for t in range(n):
+        q0, q1, kl = int(q_cu[t]), int(q_cu[t + 1]), int(k_cu[t + 1] - k_cu[t])
+        d = int(doc[t])
+        assert src[t] == cu[d] and q1 <= cu[d + 1]           # one document, context from its start
+        assert kl == q1 - cu[d]                               # context = prefix up to the run's end
+        x0 = q0 - int(cu[d])                                  # first row's index in the document
+        pairs = sum(x + 1 for x in range(x0, x0 + (q1 - q0)))
+        assert pairs <= max_pairs or q1 - q0 == 1
+        if q1 < cu[d + 1]:                                    # greedy: one more row would break the bound
+            assert pairs + (x0 + q1 - q0) + 1 > max_pairs
+    return q_cu, k_cu, src
+
+
+@pytest.mark.parametrize("lens,max_pairs", [([5, 0, 7], 10), ([1, 300, 64, 1000], 4096), ([1000], 1),
+                                            ([257, 129], 100000), ([], 5)])
+def test_cad_split_tasks_are_bounded_prefix_chunks(lens, max_pairs):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    _check_cad_split(cu, max_pairs)
+
+
+def test_cad_split_reproduces_document_causal_attention():
+    """Gathering each task's context from its document makes the task mask equal the
+    documents' causal mask row by row, with the same useful-pair count."""
+    rng = np.random.default_rng(2)
+    for _ in range(10):
+        lens = rng.integers(0, 200, int(rng.integers(1, 5)))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        max_pairs = int(rng.integers(1, 6000))
+        q_cu, k_cu, src = _check_cad_split(cu, max_pairs)
+        kv_rows = np.concatenate([np.arange(s, s + k_cu[t + 1] - k_cu[t]) for t, s in enumerate(src)]
+                                 + [np.zeros(0, np.int64)]).astype(np.int64)
+        mt = oracle.task_mask(q_cu, k_cu, True)
+        mv = oracle.varlen_mask(cu, True)
+        mapped = np.zeros_like(mv)
+        for r, j in zip(*np.nonzero(mt)):
+            assert not mapped[r, kv_rows[j]]
+            mapped[r, kv_rows[j]] = True
+        assert np.array_equal(mapped, mv)
+        if cu[-1]:
+            tp = B.Plan.tasks(q_cu, k_cu, True, 2, 1, 64).useful_pairs
+            assert tp == B.Plan.varlen(cu, True, 2, 1, 64).useful_pairs == int(mv.sum())
