@@ -14,8 +14,10 @@ Training", English abstract).  The step runs, on one HIP stream:
 The local corrupted K/V join the call of one chosen shard.  Shards whose plan
 has no legal pair are left out of the forward and the merge (their partial
 would carry LSE = -inf everywhere); their backward still runs and writes zero
-gradients.  This module only sequences calls and owns buffers; every
-arithmetic step runs in libbdattn.so.
+gradients.  When a single shard has legal pairs -- in particular when the whole
+clean K/V is resident and passed as one range -- its forward writes the bf16
+output and the LSE directly: no fp32 partial and no merge.  This module only
+sequences calls and owns buffers; every arithmetic step runs in libbdattn.so.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ from . import bdattn as B
 
 class BdlmRankStep:
     def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda",
-                 part_dtype=torch.float32, keep_partials: bool = False):
+                 part_dtype=torch.float32):
         self.problem = problem
         self.shards = list(shards)
         self.device = device
@@ -37,7 +39,9 @@ class BdlmRankStep:
         p = problem
         self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
         self.ws = B.workspace(max(pl.workspace_bytes for pl in self.plans), device)
-        n_parts = max(1, len(self.active))
+        # one active shard: its forward writes O and LSE itself (no partials)
+        self.direct = len(self.active) == 1
+        n_parts = 0 if self.direct else max(1, len(self.active))
         self.o_parts = torch.empty((n_parts, self.n_q, self.h_q, self.d), dtype=part_dtype, device=device)
         self.lse_parts = torch.empty((n_parts, self.h_q, self.n_q), dtype=torch.float32, device=device)
         self.o = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.bfloat16, device=device)
@@ -49,7 +53,6 @@ class BdlmRankStep:
         self.dv_clean = torch.empty_like(self.dk_clean)
         self.dk_corr = torch.empty((p.n_corr, self.h_kv, self.d), dtype=torch.bfloat16, device=device)
         self.dv_corr = torch.empty_like(self.dk_corr)
-        self.keep_partials = keep_partials
         self.timer = None      # optional callable(tag) -> context manager around each library call
 
     @property
@@ -65,6 +68,13 @@ class BdlmRankStep:
         if not self.active:
             self.o.zero_()
             self.lse.fill_(float("-inf"))
+            return self.o, self.lse
+        if self.direct:
+            i = self.active[0]
+            off, n, local = self.shards[i]
+            with self._t("fwd"):
+                B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
+                             k_corr if local else None, v_corr if local else None, self.o, self.lse, self.ws)
             return self.o, self.lse
         for slot, i in enumerate(self.active):
             off, n, local = self.shards[i]

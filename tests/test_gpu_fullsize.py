@@ -78,17 +78,19 @@ def bdlm_oracle_group0(cfg, inp):
     return G, rows_fwd_bwd, attending_rows
 
 
-def run_bdlm_fullsize(idx, n_rows, n_slots, n_tail_keys):
+def run_bdlm_fullsize(idx, n_rows, n_slots, n_tail_keys, fused=False):
     need_gpu()
     cfg = wl.config(idx)
     p = cfg.problem
     log(f"{cfg.name}: generating inputs")
     inp = wl.bdlm_inputs(cfg, seed=0)
     g = {k: v.cuda() for k, v in inp.items()}
-    step = BdlmRankStep(p, cfg.shards)
+    shards = [(0, p.clean_len, True)] if fused else cfg.shards
+    step = BdlmRankStep(p, shards)
+    assert step.direct == fused
     poison_(step.o_parts, step.lse_parts, step.o, step.lse, step.dq, step.dk_clean, step.dv_clean,
             step.dk_corr, step.dv_corr)
-    log(f"{cfg.name}: GPU step ({len(cfg.shards)} clean shards)")
+    log(f"{cfg.name}: GPU step ({len(shards)} clean K/V range(s))")
     step.step(g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
     torch.cuda.synchronize()
     o, lse, dq = step.o.cpu(), step.lse.cpu(), step.dq.cpu()
@@ -125,6 +127,11 @@ def run_bdlm_fullsize(idx, n_rows, n_slots, n_tail_keys):
 
 def test_csbp_256k_rank_share_fullsize():
     run_bdlm_fullsize(3, n_rows=48, n_slots=2, n_tail_keys=64)
+
+
+def test_csbp_256k_rank_share_fused_fullsize():
+    """All sixteen clean shards resident and passed as one range (no partials, no merge)."""
+    run_bdlm_fullsize(3, n_rows=48, n_slots=2, n_tail_keys=64, fused=True)
 
 
 def test_csbp_1m_rank_share_fullsize():

@@ -68,7 +68,12 @@ def test_small_rank_shares(spec):
     L, Bs, R, rank, hq, hkv, d, ns = spec
     cfg = wl.small_bdlm_config(L, Bs, R, rank, hq, hkv, d, ns)
     inp = wl.bdlm_inputs(cfg, seed=1)
-    compare_bdlm(run_gpu_bdlm(cfg, inp), oracle_bdlm_full(cfg, inp), cfg.name)
+    want = oracle_bdlm_full(cfg, inp)
+    compare_bdlm(run_gpu_bdlm(cfg, inp), want, cfg.name)
+    # every clean shard resident and passed as one range: O and LSE written by the forward itself
+    fused = run_gpu_bdlm(cfg, inp, shards=[(0, L, True)])
+    assert fused["step"].direct
+    compare_bdlm(fused, want, cfg.name + " fused whole range")
 
 
 @pytest.mark.parametrize("lens,causal,hq,hkv,d", [
