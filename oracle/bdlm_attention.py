@@ -96,6 +96,33 @@ def bdlm_mask_fn(clean_len, block_size, q_clean_offset, q_clean_len, owned_block
     return fn
 
 
+def combined_mask(clean_len: int, block_size: int, rows: Optional[np.ndarray] = None,
+                  keys: Optional[np.ndarray] = None) -> np.ndarray:
+    """The BDLM mask over the whole combined sequence, before any sharding.
+
+    Index i < L is the clean token at position i; index L + i is the corrupted
+    (noised) token at position i, which belongs to target block i // B.  This is
+    the sequence that conventional context parallelism shards by position
+    ("Block Parallelism For Efficient Distributed Long-Context Diffusion Language
+    Model Training", English abstract; rit.work explainer of CSBP, section "why
+    conventional context parallelism sends extra data"):
+
+      clean i      -> clean j      : block(j) <= block(i)
+      clean i      -> corrupted    : never
+      corrupted i  -> clean j      : block(j) <  block(i)
+      corrupted i  -> corrupted j  : block(j) == block(i)
+    """
+    L, B = int(clean_len), int(block_size)
+    rows = np.arange(2 * L, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.arange(2 * L, dtype=np.int64) if keys is None else np.asarray(keys, dtype=np.int64)
+    rc, kc = rows < L, keys < L
+    rb, kb = (rows % L) // B, (keys % L) // B
+    cc = rc[:, None] & kc[None, :] & (kb[None, :] <= rb[:, None])
+    xc = ~rc[:, None] & kc[None, :] & (kb[None, :] < rb[:, None])
+    xx = ~rc[:, None] & ~kc[None, :] & (kb[None, :] == rb[:, None])
+    return cc | xc | xx
+
+
 def varlen_mask(cu_seqlens: Sequence[int], causal: bool, rows: Optional[np.ndarray] = None,
                 keys: Optional[np.ndarray] = None) -> np.ndarray:
     """Packed independent shards: key j is legal for row i iff both lie in the same

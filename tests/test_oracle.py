@@ -571,3 +571,63 @@ def test_task_mask_matches_scalar_definition(orc):
         for j in range(k_cu[-1]):
             legal = k_cu[t] <= j < k_cu[t + 1] and (j - k_cu[t]) <= kl - ql + (i - q_cu[t])
             assert m[i, j] == legal, (i, j)
+
+
+# ----------------------------------------------------------------------------- combined sequence
+
+COMBINED = os.path.join(os.path.dirname(__file__), "golden", "combined_mask_L6_B2.txt")
+
+
+def test_combined_mask_matches_hand_derived_fixture(orc):
+    rows = [ln.strip() for ln in open(COMBINED) if ln.strip() and not ln.startswith("#")]
+    want = np.array([[c == "1" for c in r] for r in rows])
+    assert want.shape == (12, 12)
+    assert np.array_equal(orc.combined_mask(6, 2), want)
+
+
+@pytest.mark.parametrize("L,B", [(6, 2), (64, 1), (96, 8), (120, 40), (128, 128)])
+def test_combined_mask_counts_closed_form(L, B, orc):
+    """A clean row of block b sees (b+1)B clean keys; a corrupted row of block b sees
+    bB clean keys and its B own corrupted keys; all pairs: B^2 n_b (n_b + 1)."""
+    m = orc.combined_mask(L, B)
+    blk = np.arange(L) // B
+    assert np.array_equal(m[:L].sum(axis=1), (blk + 1) * B)
+    assert np.array_equal(m[L:, :L].sum(axis=1), blk * B)
+    assert np.array_equal(m[L:, L:].sum(axis=1), np.full(L, B))
+    nb = L // B
+    assert int(m.sum()) == B * B * nb * (nb + 1)
+
+
+def _rank_rows_keys(L, B, q_off, q_len, owned, kv_off, kv_len, local):
+    """Combined-sequence indices of a rank's rows and of one call's keys."""
+    owned = np.asarray(owned, dtype=np.int64)
+    corr = (L + owned[:, None] * B + np.arange(B)[None, :]).reshape(-1)
+    rows = np.concatenate([q_off + np.arange(q_len), corr]).astype(np.int64)
+    keys = np.concatenate([kv_off + np.arange(kv_len), corr if local else np.zeros(0, np.int64)]).astype(np.int64)
+    return rows, keys
+
+
+@pytest.mark.parametrize("L,B,R", [(96, 4, 2), (128, 8, 4), (64, 1, 4)])
+def test_rank_shares_partition_the_combined_mask(L, B, R, orc):
+    """Both position shardings -- CSBP (clean shard r, zigzag corrupted blocks) and
+    conventional CP (clean and corrupted positions of chunk r) -- give every row of
+    the combined sequence to exactly one rank; each rank's call against clean shard s
+    (plus its own corrupted K/V) is the combined mask restricted to those rows and
+    keys; and no rank's row may attend another rank's corrupted keys."""
+    full = orc.combined_mask(L, B)
+    nb, n = L // B, L // R
+    for scheme in ("csbp", "cp"):
+        seen = np.zeros(2 * L, dtype=int)
+        for r in range(R):
+            owned = (wl.zigzag_owned_blocks(nb, R, r) if scheme == "csbp"
+                     else np.arange(r * nb // R, (r + 1) * nb // R))
+            rows, own_keys = _rank_rows_keys(L, B, r * n, n, owned, 0, 0, True)
+            seen[rows] += 1
+            for s in range(R):
+                local = s == r
+                m = orc.bdlm_mask(L, B, r * n, n, owned, s * n, n, local)
+                _, keys = _rank_rows_keys(L, B, r * n, n, owned, s * n, n, local)
+                assert np.array_equal(m, full[np.ix_(rows, keys)]), (scheme, r, s)
+            other_corr = np.setdiff1d(np.arange(L, 2 * L), own_keys)
+            assert not full[np.ix_(rows, other_corr)].any(), (scheme, r)
+        assert np.all(seen == 1), scheme

@@ -35,6 +35,11 @@ MUTATIONS = [
      "lse = np.where(has, np.log(np.where(has, tot, 1.0)), NEG_INF)"),
     ("varlen_strict_causal", "m &= keys[None, :] <= rows[:, None]", "m &= keys[None, :] < rows[:, None]"),
     ("delta_transposed_heads", 'np.einsum("nhd,nhd->hn"', 'np.einsum("nhd,nhd->nh"'),
+    ("combined_corrupted_sees_own_clean_block", "xc = ~rc[:, None] & kc[None, :] & (kb[None, :] < rb[:, None])",
+     "xc = ~rc[:, None] & kc[None, :] & (kb[None, :] <= rb[:, None])"),
+    ("combined_corrupted_sees_earlier_corrupted", "xx = ~rc[:, None] & ~kc[None, :] & (kb[None, :] == rb[:, None])",
+     "xx = ~rc[:, None] & ~kc[None, :] & (kb[None, :] <= rb[:, None])"),
+    ("combined_position_not_wrapped", "rb, kb = (rows % L) // B, (keys % L) // B", "rb, kb = rows // B, keys // B"),
     ("task_top_left_causal", "limit = kc[tr] + k_len - q_len + (rows - qc[tr]) + 1",
      "limit = kc[tr] + (rows - qc[tr]) + 1"),
     ("task_strict_causal", "limit = kc[tr] + k_len - q_len + (rows - qc[tr]) + 1",
