@@ -207,6 +207,19 @@ def bench_varlen(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def exchange_report(p, scheme: str, ranks: int):
+    """K/V bytes this rank receives per step (its gradients go back in the backward) and the
+    balance of attention work over all ranks, for this rank's scheme and the other one."""
+    from masked_long_context_amd import exchange
+    rank = p.q_clean_offset // (p.clean_len // ranks)
+    c = exchange.compare_schemes(p.clean_len, p.block_size, ranks, p.h_kv, p.head_dim)
+    mine = c["ranks"][scheme][rank]
+    return {"scheme": scheme, "rank": rank, "ranks": ranks,
+            "kv_bytes_received": mine.kv_bytes_received, "kv_bytes_needed": mine.kv_bytes_needed,
+            "remote_clean_shards_needed": mine.remote_clean_needed,
+            "per_scheme": c["summary"]}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -221,9 +234,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6],
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7],
                     help="workload: 3 = the 256K rank share (default); 4 = varlen packed causal shards; "
-                         "6 = workload 4's documents as core-attention tasks with prefix contexts")
+                         "6 = workload 4's documents as core-attention tasks with prefix contexts; "
+                         "7 = conventional context parallelism's share of the same 256K sequence")
     ap.add_argument("--fused", action="store_true",
                     help="workloads 1-3, 5: pass the whole clean K/V as one range (all shards resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -328,6 +342,8 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    if args.config in (3, 7):
+        out["exchange"] = exchange_report(p, "cp" if args.config == 7 else "csbp", len(cfg.shards))
     if not args.no_cpu_baseline:
         print(f"# bench: cpu baseline (oracle, {args.cpu_rows} sampled rows)", file=sys.stderr, flush=True)
         dt, spairs, nrows = cpu_baseline_bdlm(cfg, inp, args.cpu_rows)

@@ -171,6 +171,16 @@ def zigzag_owned_blocks(n_blocks: int, ranks: int, rank: int) -> np.ndarray:
     return np.concatenate([early, late])
 
 
+def cp_owned_blocks(n_blocks: int, ranks: int, rank: int) -> np.ndarray:
+    """Corrupted blocks of ``rank`` under conventional context parallelism: the
+    position chunk [rank * n, (rank + 1) * n) of the corrupted copy, n = N_b / R,
+    the same positions as the rank's clean chunk."""
+    if n_blocks % ranks != 0:
+        raise ValueError("n_blocks must be a multiple of ranks")
+    n = n_blocks // ranks
+    return np.arange(rank * n, (rank + 1) * n, dtype=np.int64)
+
+
 def varlen_lengths(total: int = 262144, lo: int = 128, hi: int = 65536, seed: int = 0) -> List[int]:
     """Shard lengths log-uniform in [lo, hi] that sum exactly to ``total``.
 
@@ -194,9 +204,10 @@ def varlen_lengths(total: int = 262144, lo: int = 128, hi: int = 65536, seed: in
     return out
 
 
-def _bdlm_config(name, L, B, R, rank, hq, hkv, d, scale, n_shards, local_shard, desc) -> BdlmConfig:
+def _bdlm_config(name, L, B, R, rank, hq, hkv, d, scale, n_shards, local_shard, desc,
+                 ownership=None) -> BdlmConfig:
     n_blocks = L // B
-    owned = zigzag_owned_blocks(n_blocks, R, rank)
+    owned = (ownership or zigzag_owned_blocks)(n_blocks, R, rank)
     q_off = rank * (L // R)
     q_len = L // R
     prob = BdlmProblem(clean_len=L, block_size=B, q_clean_offset=q_off, q_clean_len=q_len,
@@ -208,8 +219,9 @@ def _bdlm_config(name, L, B, R, rank, hq, hkv, d, scale, n_shards, local_shard, 
 
 
 def config(idx: int):
-    """Workloads 1..6 (1: tiny, 2: 4K GQA, 3: 256K/16 rank share, 4: varlen, 5: 1M/8 rank share,
-    6: workload 4 as core-attention tasks with prefix context)."""
+    """Workloads 1..7 (1: tiny, 2: 4K GQA, 3: 256K/16 rank share, 4: varlen, 5: 1M/8 rank share,
+    6: workload 4 as core-attention tasks with prefix context, 7: conventional CP's share of the
+    256K combined sequence, rank 8 of 16)."""
     if idx == 1:
         return _bdlm_config("tiny_L256_B32_h1_d64", 256, 32, 1, 0, 1, 1, 64, 1.0, 1, 0,
                             "L=256, B=32, 1/1 heads, d=64, unsharded, all 8 blocks")
@@ -227,6 +239,11 @@ def config(idx: int):
     if idx == 5:
         return _bdlm_config("csbp_1M_r4of8_B16_h32x8_d128", 1048576, 16, 8, 4, 32, 8, 128, 1.0,
                             8, 4, "1M clean context split 8 ways, rank 4, B=16, 32/8 heads, d=128")
+    if idx == 7:
+        return _bdlm_config("cp_256K_r8of16_B32_h32x8_d128", 262144, 32, 16, 8, 32, 8, 128, 1.0, 16, 8,
+                            "conventional context parallelism's share of the 256K combined sequence: "
+                            "rank 8 of 16 holds positions [131072, 147456) of both copies",
+                            ownership=cp_owned_blocks)
     if idx == 6:
         return CadTaskConfig(name="cad_tasks_262144_max2p26_h32x8_d128", docs=config(4), max_pairs=1 << 26,
                              description="workload 4's documents as core-attention tasks of at most 2^26 "
@@ -234,12 +251,13 @@ def config(idx: int):
     raise ValueError(idx)
 
 
-def small_bdlm_config(L, B, R, rank, hq, hkv, d, n_shards, scale=1.0, name=None) -> BdlmConfig:
-    """A scaled-down CSBP rank share with the same structure as the large workloads."""
-    n_blocks = L // B
+def small_bdlm_config(L, B, R, rank, hq, hkv, d, n_shards, scale=1.0, name=None, cp=False) -> BdlmConfig:
+    """A scaled-down rank share with the same structure as the large workloads (CSBP's
+    zigzag ownership, or with cp=True conventional context parallelism's position chunk)."""
     local = min(rank * n_shards // R, n_shards - 1)
-    return _bdlm_config(name or f"small_L{L}_B{B}_R{R}_r{rank}", L, B, R, rank, hq, hkv, d, scale,
-                        n_shards, local, "scaled-down rank share")
+    return _bdlm_config(name or f"small_{'cp' if cp else 'csbp'}_L{L}_B{B}_R{R}_r{rank}", L, B, R, rank, hq,
+                        hkv, d, scale, n_shards, local, "scaled-down rank share",
+                        ownership=cp_owned_blocks if cp else None)
 
 
 # ----------------------------------------------------------------------------- tensors

@@ -134,6 +134,11 @@ def test_csbp_256k_rank_share_fused_fullsize():
     run_bdlm_fullsize(3, n_rows=48, n_slots=2, n_tail_keys=64, fused=True)
 
 
+def test_cp_256k_rank_share_fullsize():
+    """Conventional context parallelism's share of the same sequence (rank 8's position chunk)."""
+    run_bdlm_fullsize(7, n_rows=48, n_slots=2, n_tail_keys=64)
+
+
 def test_csbp_1m_rank_share_fullsize():
     run_bdlm_fullsize(5, n_rows=16, n_slots=2, n_tail_keys=32)
 

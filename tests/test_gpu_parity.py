@@ -76,6 +76,19 @@ def test_small_rank_shares(spec):
     compare_bdlm(fused, want, cfg.name + " fused whole range")
 
 
+@pytest.mark.parametrize("spec", [(512, 16, 4, 3, 4, 2, 128, 4), (768, 32, 2, 0, 2, 1, 64, 3),
+                                  (1600, 200, 4, 2, 2, 2, 64, 4)],
+                         ids=lambda s: "L{}_B{}_R{}_r{}_h{}x{}_d{}_s{}".format(*s))
+def test_small_cp_shares(spec):
+    """Conventional context parallelism's share: the rank's clean and corrupted positions of
+    one chunk, against every clean shard (remote corrupted chunks hold no legal key)."""
+    L, Bs, R, rank, hq, hkv, d, ns = spec
+    cfg = wl.small_bdlm_config(L, Bs, R, rank, hq, hkv, d, ns, cp=True)
+    assert list(cfg.problem.owned_blocks) == list(wl.cp_owned_blocks(L // Bs, R, rank))
+    inp = wl.bdlm_inputs(cfg, seed=7)
+    compare_bdlm(run_gpu_bdlm(cfg, inp), oracle_bdlm_full(cfg, inp), cfg.name)
+
+
 @pytest.mark.parametrize("lens,causal,hq,hkv,d", [
     ([1, 5, 130, 64, 257, 300], True, 4, 2, 128),
     ([7, 129, 128, 1, 600], False, 2, 1, 64),
