@@ -60,6 +60,8 @@ SMALL = [
     (1024, 128, 2, 1, 2, 1, 128, 2),
     (1600, 200, 2, 1, 2, 2, 64, 4),
     (2048, 32, 8, 5, 8, 2, 128, 8),
+    (1024, 32, 4, 2, 8, 1, 128, 4),     # GQA group of 8 q-heads per KV head
+    (768, 16, 2, 1, 16, 2, 64, 3),      # group of 8, d = 64
 ]
 
 
@@ -93,14 +95,16 @@ def test_small_cp_shares(spec):
     ([1, 5, 130, 64, 257, 300], True, 4, 2, 128),
     ([7, 129, 128, 1, 600], False, 2, 1, 64),
     ([0, 70, 0, 200], True, 4, 4, 64),
+    ([33, 200, 511], True, 8, 1, 128),     # GQA group of 8
 ])
 def test_varlen_small(lens, causal, hq, hkv, d):
     """Shards of length 0, 1 and 5 concentrate attention (dV of a length-1 shard is dO itself),
-    so dO is halved to keep |outputs| < 4, where the 2e-2 bound is above bf16 output resolution."""
+    so dO is halved to keep |outputs| < 4, where the 2e-2 bound is above bf16 output resolution;
+    dV sums the q-heads of a KV head, so a group of 8 quarters dO instead."""
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cfg = wl.VarlenConfig("t", tuple(lens), hq, hkv, d, causal, 1.0, "")
     inp = wl.varlen_inputs(cfg, seed=2)
-    inp["dout"] = (inp["dout"].float() * 0.5).to(torch.bfloat16)
+    inp["dout"] = (inp["dout"].float() * (0.5 if hq // hkv <= 4 else 0.25)).to(torch.bfloat16)
     got = run_gpu_varlen(cu, causal, hq, hkv, d, inp)
     want = oracle_varlen(cu, causal, cfg.scale, inp)
     check_lse("lse", got["lse"], want["lse"])
@@ -113,13 +117,14 @@ def test_varlen_small(lens, causal, hq, hkv, d):
     ([70, 5, 300], [10, 0, 129], True, 2, 1, 64),                       # leading rows without keys; no keys
     ([0, 40, 0, 65], [12, 40, 0, 300], True, 4, 4, 64),                 # tasks without queries or keys
     ([7, 129, 128, 1], [300, 33, 128, 64], False, 2, 1, 128),
+    ([100, 257, 64], [600, 257, 40], True, 8, 1, 64),                   # group of 8, d = 64
 ])
 def test_tasks_small(q_lens, k_lens, causal, hq, hkv, d):
-    """Core-attention tasks with their own contexts (bottom-right causal); dO halved as for varlen."""
+    """Core-attention tasks with their own contexts (bottom-right causal); dO scaled as for varlen."""
     q_cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     k_cu = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32)
     inp = wl.task_inputs(int(q_cu[-1]), int(k_cu[-1]), hq, hkv, d, seed=3)
-    inp["dout"] = (inp["dout"].float() * 0.5).to(torch.bfloat16)
+    inp["dout"] = (inp["dout"].float() * (0.5 if hq // hkv <= 4 else 0.25)).to(torch.bfloat16)
     print(f"tasks q={q_lens} k={k_lens} causal={causal} heads {hq}/{hkv} d={d}", flush=True)
     got = run_gpu_tasks(q_cu, k_cu, causal, hq, hkv, d, inp)
     want = oracle_tasks(q_cu, k_cu, causal, 1.0 / np.sqrt(d), inp)
