@@ -66,9 +66,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, const void *op,
     for (int s = 0; s < n_parts; ++s) tot += expf(lp[s * lstride + lidx] - m);
     lse = m + logf(tot);
     const int64_t ostride = n_rows * h * D;
-    for (int s = 0; s < n_parts; ++s) {
-      const float c = expf(lp[s * lstride + lidx] - lse);
-      if (c == 0.f) continue;
+    auto part = [&](int s) {
       f32x4 v;
       if (parts_f32) {
         v = *reinterpret_cast<const f32x4 *>((const float *)op + s * ostride + oidx);
@@ -77,6 +75,30 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, const void *op,
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (float)b[i];
       }
+      return v;
+    };
+    // Partials in groups of four: the group's weights first, then its loads, all
+    // issued before any is used, so that each lane keeps up to four loads in
+    // flight.  A partial of weight 0 (LSE = -inf, or negligible) is not loaded:
+    // its lanes are masked off and move no data.
+    constexpr int U = 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + U <= n_parts; s += U) {
+      float c[U];
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = expf(lp[(s + u) * lstride + lidx] - lse);
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = c[u] != 0.f ? part(s + u) : zero;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(c[u], v[u][i], acc[i]);
+    }
+    for (; s < n_parts; ++s) {
+      const float c = expf(lp[s * lstride + lidx] - lse);
+      const f32x4 v = c != 0.f ? part(s) : zero;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(c, v[i], acc[i]);
     }
