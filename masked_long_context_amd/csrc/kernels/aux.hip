@@ -42,28 +42,47 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   if (valid && sub == 0) a.delta[(int64_t)h * a.n_q + r] = dot;
 }
 
+// Partial LSEs a merge workgroup stages in LDS (more partials read them from
+// global memory).
+constexpr int kMergeStage = 64;
+
 // D/4 lanes per (row, head); each lane merges 4 consecutive elements.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(int n_parts, const void *op, int parts_f32,
                                                     const float *lp, int64_t n_rows, int h, void *oo,
                                                     int out_f32, float *lo) {
   constexpr int LPR = D / 4;
+  constexpr int PAIRS = 256 / LPR;   // (row, head) pairs of the workgroup
+  __shared__ float sl[kMergeStage][PAIRS];
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t rh = gid / LPR;
   const int sub = (int)(gid % LPR);
-  if (rh >= n_rows * h) return;
+  const int pair = threadIdx.x / LPR;
+  const int64_t n_rh = n_rows * h;
+  const int64_t lstride = (int64_t)h * n_rows;
+  // the workgroup's partial LSEs, read once into LDS
+  const bool staged = n_parts <= kMergeStage;
+  if (staged) {
+    for (int i = threadIdx.x; i < n_parts * PAIRS; i += 256) {
+      const int s = i / PAIRS, pr = i % PAIRS;
+      const int64_t r2 = (int64_t)blockIdx.x * PAIRS + pr;
+      sl[s][pr] = r2 < n_rh ? lp[s * lstride + (r2 % h) * n_rows + r2 / h] : -INFINITY;
+    }
+    __syncthreads();
+  }
+  if (rh >= n_rh) return;
   const int64_t n = rh / h;
   const int hh = (int)(rh % h);
-  const int64_t lstride = (int64_t)h * n_rows;
   const int64_t lidx = (int64_t)hh * n_rows + n;
+  auto lse_of = [&](int s) { return staged ? sl[s][pair] : lp[s * lstride + lidx]; };
   float m = -INFINITY;
-  for (int s = 0; s < n_parts; ++s) m = fmaxf(m, lp[s * lstride + lidx]);
+  for (int s = 0; s < n_parts; ++s) m = fmaxf(m, lse_of(s));
   const int64_t oidx = rh * D + 4 * sub;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (m != -INFINITY) {
     float tot = 0.f;
-    for (int s = 0; s < n_parts; ++s) tot += expf(lp[s * lstride + lidx] - m);
+    for (int s = 0; s < n_parts; ++s) tot += expf(lse_of(s) - m);
     lse = m + logf(tot);
     const int64_t ostride = n_rows * h * D;
     auto part = [&](int s) {
@@ -88,7 +107,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, const void *op,
       float c[U];
       f32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) c[u] = expf(lp[(s + u) * lstride + lidx] - lse);
+      for (int u = 0; u < U; ++u) c[u] = expf(lse_of(s + u) - lse);
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = c[u] != 0.f ? part(s + u) : zero;
 #pragma unroll
@@ -97,7 +116,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, const void *op,
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(c[u], v[u][i], acc[i]);
     }
     for (; s < n_parts; ++s) {
-      const float c = expf(lp[s * lstride + lidx] - lse);
+      const float c = expf(lse_of(s) - lse);
       const f32x4 v = c != 0.f ? part(s) : zero;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(c, v[i], acc[i]);

@@ -166,8 +166,11 @@ def test_cad_tasks_reproduce_document_attention():
 
 @pytest.mark.parametrize("S,N,H,d,pdt,odt", [(5, 1000, 3, 128, torch.float32, torch.bfloat16),
                                              (3, 77, 2, 64, torch.float32, torch.float32),
-                                             (4, 300, 4, 128, torch.bfloat16, torch.float32)])
+                                             (4, 300, 4, 128, torch.bfloat16, torch.float32),
+                                             (64, 130, 3, 128, torch.float32, torch.bfloat16),
+                                             (70, 90, 2, 64, torch.float32, torch.float32)])
 def test_lse_merge_kernel(S, N, H, d, pdt, odt):
+    """Up to 64 partials are merged from LSEs staged in LDS, more from global memory."""
     o, lse = wl.merge_partials_inputs(S, N, H, d, seed=3, neg_inf_frac=0.3)
     lse[:, 0, :5] = float("-inf")           # rows with every partial empty
     o_in = o.to(pdt)
