@@ -9,16 +9,19 @@ namespace bdattn {
 namespace {
 
 // delta[h][r] = <dO[r][h], O[r][h]> (fp32), and the optional clear of the dQ
-// accumulator.  D/8 threads per (row, head), each on 8 consecutive elements.
+// accumulator.  D/8 threads per (row, head), each on 8 consecutive elements;
+// the (row, head) pairs are taken in memory order, so a wave reads and writes
+// one contiguous span.
 template <int D>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   constexpr int TPR = D / 8;
-  const int tid = threadIdx.x, h = blockIdx.y;
-  const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + tid / TPR;
-  const int sub = tid % TPR;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rh = gid / TPR;              // (row, head) in memory order
+  const int sub = (int)(gid % TPR);
+  const int64_t n_rh = (int64_t)a.n_q * a.h_q;
   float dot = 0.f;
-  const bool valid = r < a.n_q;
-  const int64_t off = (r * a.h_q + h) * D + sub * 8;
+  const bool valid = rh < n_rh;
+  const int64_t off = rh * D + sub * 8;
   if (valid) {
     const bf16x8 db = ld_bf16x8((const bf16 *)a.dout + off);
     if (a.o_f32) {
@@ -39,7 +42,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, TPR);
-  if (valid && sub == 0) a.delta[(int64_t)h * a.n_q + r] = dot;
+  if (valid && sub == 0) {
+    const int64_t r = rh / a.h_q;
+    const int h = (int)(rh % a.h_q);
+    a.delta[(int64_t)h * a.n_q + r] = dot;
+  }
 }
 
 // Partial LSEs a merge workgroup stages in LDS (more partials read them from
@@ -154,10 +161,10 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float *acc, bf16
 
 hipError_t launch_prepare(const PrepArgs &a, int32_t d, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
-  const int rows_per_block = 256 / (d / 8);
-  dim3 grid((unsigned)((a.n_q + rows_per_block - 1) / rows_per_block), (unsigned)a.h_q);
-  if (d == 128) hipLaunchKernelGGL(prepare_kernel<128>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(prepare_kernel<64>, grid, dim3(256), 0, s, a);
+  const int64_t threads = (int64_t)a.n_q * a.h_q * (d / 8);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (d == 128) hipLaunchKernelGGL(prepare_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(prepare_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
