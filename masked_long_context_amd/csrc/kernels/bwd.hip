@@ -119,31 +119,31 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
     return x;
   };
   u32x4 rec1 = {0u, 0u, 0u, 0u}, rec2 = {0u, 0u, 0u, 0u};   // records of tiles i + 1 and i + 2
-  // Loads of iteration i: Q(i + 2) and dO(i + 1), each with side rows.  The side
-  // rows (one dword per lane) are issued at the start of the iteration.  Wave 0
-  // fetches the Q tile's LSE into a register; lse_store() later puts the exponent
-  // offset -LSE log2(e) into the side rows (FLT_MAX for a row without keys,
-  // LSE = -inf, so that exp2(-inf + offset) is still 0).  Waves 2 and 3 fetch the
-  // rows' legal key bounds, wave 1 the dO tile's delta.  The tile loads (1 KB per
-  // instruction) are issued by the dK waves alone: a wave stalls at issue until
-  // the CU's vector memory path accepts its loads, and the dK waves have the
-  // slack (their iteration is shorter than the dV waves', which carry the
-  // exponentials).
+  // Loads of iteration i: Q(i + 2) and dO(i + 1), each with side rows.  Every
+  // load is issued by the dK waves (4..7): a wave stalls at issue until the CU's
+  // vector memory path accepts its loads, and the dK waves have the slack (their
+  // iteration is shorter than the dV waves', which carry the exponentials).  The
+  // side rows (one dword per lane) are issued at the start of the iteration.
+  // Wave 4 fetches the Q tile's LSE into a register; lse_store() later puts the
+  // exponent offset -LSE log2(e) into the side rows (FLT_MAX for a row without
+  // keys, LSE = -inf, so that exp2(-inf + offset) is still 0).  Waves 6 and 7
+  // fetch the rows' legal key bounds, wave 5 the dO tile's delta.  The tile loads
+  // take 1 KB per instruction.
   float lse_reg = 0.f;
   auto side_q = [&](const TileRef &r, int b) {
     const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
-    if (wave == 0) {
+    if (wave == 4) {
       lse_reg = a.lse[(int64_t)r.h * a.n_q + row];
-    } else if (wave == 2 || wave == 3) {
-      __builtin_amdgcn_global_load_lds(a.rows + (int64_t)row * 4 + 2 * s + (wave - 2), BD_LDS(&L.sq[b][wave - 1][0]),
+    } else if (wave == 6 || wave == 7) {
+      __builtin_amdgcn_global_load_lds(a.rows + (int64_t)row * 4 + 2 * s + (wave - 6), BD_LDS(&L.sq[b][wave - 5][0]),
                                        4, 0, 0);
     }
   };
-  auto lse_store = [&](int b) {   // wave 0, once its loads have landed
-    if (wave == 0) L.sq[b][0][lane] = fminf(-lse_reg * kLog2e, FLT_MAX);
+  auto lse_store = [&](int b) {   // wave 4, once its loads have landed
+    if (wave == 4) L.sq[b][0][lane] = fminf(-lse_reg * kLog2e, FLT_MAX);
   };
   auto side_d = [&](const TileRef &r, int b) {
-    if (wave == 1) {
+    if (wave == 5) {
       const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
       __builtin_amdgcn_global_load_lds(a.delta + (int64_t)r.h * a.n_q + row, BD_LDS(L.sd[b]), 4, 0, 0);
     }
