@@ -40,10 +40,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libbdattn.so)")
 
 
-# Per-source scheduler choice: the backward kernels gain from LLVM's ILP-first
-# machine scheduler (operand loads hoisted further ahead of their MFMAs); the
-# forward keeps the default, which measured faster for it.
-EXTRA = {"kernels/bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source scheduler choice: the attention kernels gain from LLVM's ILP-first
+# machine scheduler (operand loads hoisted further ahead of their MFMAs).  Of
+# the other strategies, max-memory-clause and iterative-ilp measured slower.
+ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA = {"kernels/bwd.hip": ILP, "kernels/fwd.hip": ILP}
 
 
 def _compile(src: str, resource_usage: bool, verbose: bool) -> str:
