@@ -191,12 +191,15 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
           const u32x4 lo4 = *reinterpret_cast<const u32x4 *>(&side[1][qb]);
           const u32x4 hi4 = *reinterpret_cast<const u32x4 *>(&side[2][qb]);
           const int left = r.nrows - qb;                  // rows qb + i with i < left exist
+          // integer sign test (no per-element lane masks): the pair is illegal
+          // iff one of left - 1 - i, key - lo, hi - 1 - key is negative; an
+          // illegal score gets -inf added, a legal one +0
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const bool ok = (i < left) & (key[kt] >= (int)lo4[i]) & (key[kt] < (int)hi4[i]);
-              if (!ok) sc[h2][kt][4 * s4 + i] = -INFINITY;
+              const int out = ((left - 1 - i) | (key[kt] - (int)lo4[i]) | ((int)hi4[i] - 1 - key[kt])) >> 31;
+              sc[h2][kt][4 * s4 + i] += __int_as_float(out & (int)0xff800000u);
             }
         }
     }
@@ -490,14 +493,18 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void d
     pipeline_lds_mfma<4 * NC, 1, 4>();
     if (!full) {
       keep_branch();
-      // illegal pairs get S = -inf, hence P = 0
-      const int lo_r = lo - k0 - 4 * g, hi_r = hi - k0 - 4 * g;
+      // illegal pairs get S = -inf, hence P = 0.  Key k0 + 4 g + o (o an
+      // immediate) is legal iff lo <= key < hi; the test is integer arithmetic
+      // (sign of (o - lo) | (hi - 1 - o)) and adds -inf or +0, so no
+      // per-element lane masks are formed.
+      const int lo_r = lo - k0 - 4 * g, hi_r = hi - 1 - k0 - 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int o = kt * 32 + 8 * (r >> 2) + (r & 3);
-          if (o < lo_r || o >= hi_r) sc[kt][r] = -INFINITY;
+          const int out = ((o - lo_r) | (hi_r - o)) >> 31;   // -1 if illegal, else 0
+          sc[kt][r] += __int_as_float(out & (int)0xff800000u);
         }
     }
 #pragma unroll

@@ -118,14 +118,17 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
     pipeline_lds_mfma<NKT * NC, 1, 4>();
     if (!full) {
       keep_branch();
-      // key k0 + 4 g + o (o an immediate) is legal iff lo <= key < hi
-      const int lo_r = lo - k0 - 4 * g, hi_r = hi - k0 - 4 * g;
+      // key k0 + 4 g + o (o an immediate) is legal iff lo <= key < hi.  The
+      // test is integer arithmetic (sign of (o - lo) | (hi - 1 - o)) and adds
+      // -inf to an illegal score, so no per-element lane masks are formed.
+      const int lo_r = lo - k0 - 4 * g, hi_r = hi - 1 - k0 - 4 * g;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int o = kt * 32 + 8 * (r >> 2) + (r & 3);
-          if (o < lo_r || o >= hi_r) sc[kt][r] = -INFINITY;
+          const int out = ((o - lo_r) | (hi_r - o)) >> 31;       // -1 if illegal, else 0
+          sc[kt][r] += __int_as_float(out & (int)0xff800000u);     // -inf or +0
         }
     }
     float mx = -INFINITY;
