@@ -136,7 +136,13 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      // the other half of the query's keys sits 32 lanes away: v_permlane32_swap
+      // of a register with itself gives every lane both halves' values (a VALU
+      // op, where a shuffle would go through the LDS crossbar)
+      const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(hv[0]), __uint_as_float(hv[1]));
+    }
     const float mx2 = mx * a.scale_log2;
     if (__any(mx2 > m_used + 8.f)) {
       const float m_new = fmaxf(m_used, mx2);
