@@ -140,6 +140,36 @@ def merge_microbench(p, n_parts: int = 16, reps: int = 5):
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def gemm_ceiling(n: int = 8192, seconds: float = 1.0):
+    """Sustained bf16 MFMA rate this GPU delivers on a plain dense contraction: the
+    vendor GEMM (torch.matmul, which dispatches to hipBLASLt) on N(0, 1) operands,
+    repeated for about `seconds` after a warm-up.  Under a long load the chip holds
+    its clock to its power budget, and operand values set the MFMA power, so this
+    rate (not the published peak) is what any bf16 MFMA kernel can sustain here."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn((n, n), generator=gen, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps, t0 = 0, time.perf_counter()
+    e0.record()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            torch.matmul(a, b)
+        reps += 8
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"kind": f"vendor bf16 GEMM (torch.matmul -> hipBLASLt), {n}^3, N(0,1) operands, {reps} reps",
+            "ms": round(ms, 1), "tflops": round(2.0 * n ** 3 * reps / (ms * 1e-3) / 1e12, 1)}
+
+
 def bench_varlen(args, cfg):
     """The varlen workload (packed token-causal shards) or its core-attention task
     form (the same documents cut into tasks that carry their prefix context,
@@ -242,6 +272,8 @@ def main():
                     help="workloads 1-3, 5: pass the whole clean K/V as one range (all shards resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the sustained-MFMA ceiling measurement (vendor bf16 GEMM, about 1 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -316,6 +348,8 @@ def main():
         torch.cuda.synchronize()
         print(f"# bench: copy calibration moved {src.numel() * 4} bytes each way", file=sys.stderr, flush=True)
 
+    ceiling = None if args.no_ceiling else gemm_ceiling()
+
     metric = METRIC if args.config == 3 else f"BDLM attention fwd+bwd useful-pair TFLOP/s and % bf16 MFMA peak, {cfg.name}"
     if args.fused:
         metric += " (all clean K/V resident, one fused range)"
@@ -332,6 +366,9 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(workload), "ms_per_launch": round(dk["ms_per_launch"], 4),
                      "flops_per_launch": dk_flops_per_launch},
+        # MFMA work the kernels execute per useful pair and q-head: 4d forward, 8d dK/dV,
+        # 6d dQ (S and dP recomputed); 14d of it is counted in `value`
+        "executed_tflops": round(pairs * p.h_q * 18 * p.head_dim / (ms * 1e-3) / 1e12, 2),
         "kernels": {
             **{k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
             "merge": {"ms": round(merge_ms / max(merge_n, 1), 4), "parts": n_act, "gbs": round(merge_gbs, 1),
@@ -342,6 +379,10 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    if ceiling is not None:
+        ceiling["dominant_kernel_frac"] = round(dk_achieved / ceiling["tflops"], 4)
+        ceiling["step_executed_frac"] = round(out["executed_tflops"] / ceiling["tflops"], 4)
+        out["roofline"]["sustained_ceiling"] = ceiling
     if args.config in (3, 7):
         out["exchange"] = exchange_report(p, "cp" if args.config == 7 else "csbp", len(cfg.shards))
     if not args.no_cpu_baseline:

@@ -135,8 +135,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
     if (wave == 4) {
       lse_reg = a.lse[(int64_t)r.h * a.n_q + row];
     } else if (wave == 6 || wave == 7) {
-      __builtin_amdgcn_global_load_lds(a.rows + (int64_t)row * 4 + 2 * s + (wave - 6), BD_LDS(&L.sq[b][wave - 5][0]),
-                                       4, 0, 0);
+      dword_load_lds(a.rows, a.n_q * 16, (row * 4 + 2 * s + (wave - 6)) * 4, &L.sq[b][wave - 5][0]);
     }
   };
   auto lse_store = [&](int b) {   // wave 4, once its loads have landed
@@ -145,7 +144,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   auto side_d = [&](const TileRef &r, int b) {
     if (wave == 5) {
       const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
-      __builtin_amdgcn_global_load_lds(a.delta + (int64_t)r.h * a.n_q + row, BD_LDS(L.sd[b]), 4, 0, 0);
+      dword_load_lds(a.delta + (int64_t)r.h * a.n_q, a.n_q * 4, row * 4, L.sd[b]);
     }
   };
   auto tile_q = [&](const TileRef &r, int b) {

@@ -18,6 +18,10 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 template <int D>
 using Tile = TileShape<D>;
 
+// Word 3 of a raw buffer resource on gfx9 (CDNA): 32-bit data format, no
+// swizzle, no index stride; offsets past num_records read as zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // This wave's share of the asynchronous copy of 64 rows starting at `g` (a
 // wave-uniform pointer; row stride `stride` elements, 64 * stride < 2^30).  Rows
 // at or beyond `nvalid` re-read row nvalid - 1 (the caller masks them);
@@ -26,16 +30,29 @@ template <int D, int NW>
 __device__ __forceinline__ void tile_load(char *lds, const bf16 *g, int stride, int nvalid, int wave, int lane) {
   constexpr int PER = Tile<D>::LOADS / NW;
   static_assert(Tile<D>::LOADS % NW == 0, "tile loads must split evenly over the waves");
-  const char *gb = reinterpret_cast<const char *>(g);
+  // A raw buffer resource over the rows the tile may touch.  The buffer form of
+  // the LDS DMA (unlike the global form) leaves the compiler's LDS read
+  // counter in order, so the operand reads that follow keep exact waits.
+  const int nrec = (nvalid < Tile<D>::ROWS ? nvalid : Tile<D>::ROWS) * stride * 2;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16 *>(g), (short)0, nrec, kBufferWord3);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int kb = wave * PER + i;
     int row, c;
     tile_load_src<D>(kb, lane, &row, &c);
     const int rr = row < nvalid ? row : nvalid - 1;
-    const uint32_t off = (uint32_t)(rr * stride + c * 8) * 2u;
-    __builtin_amdgcn_global_load_lds(gb + off, BD_LDS(lds + kb * 1024), 16, 0, 0);
+    const int off = (rr * stride + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, BD_LDS(lds + kb * 1024), 16, off, 0, 0, 0);
   }
+}
+
+// One dword per lane, from byte offset `off` of [base, base + bytes), into LDS at
+// lds + 4 * lane (the buffer form of the LDS DMA, for the reason above).
+__device__ __forceinline__ void dword_load_lds(const void *base, int bytes, int off, void *lds) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, BD_LDS(lds), 4, off, 0, 0, 0);
 }
 
 // Wave index as a scalar (uniform) value.
