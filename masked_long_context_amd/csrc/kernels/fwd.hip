@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) sc[kt] = mfma32(rd(kt_lds + (kt >> 1) * TB, kt & 1, c), qf[c], sc[kt]);
-    pipeline_lds_mfma<NKT * NC, 1, 4>();
+    pipeline_lds_mfma<NKT * NC, 1, 8>();   // eight K operands ahead (four measured 0.3-0.5% slower)
     if (!full) {
       keep_branch();
       // key k0 + 4 g + o (o an immediate) is legal iff lo <= key < hi.  The
