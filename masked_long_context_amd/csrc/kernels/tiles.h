@@ -1,8 +1,8 @@
 // LDS tiles for the gfx950 attention kernels.
 //
 // A tile is 64 rows of a row-major bf16 matrix with D elements per row, copied
-// from global memory straight into LDS by global_load_lds_dwordx4 (each lane
-// of a wave moves 16 bytes; a wave-wide load fills 1 KB of LDS in lane order),
+// from global memory straight into LDS by buffer_load_dwordx4 ... lds (each
+// lane of a wave moves 16 bytes; a wave-wide load fills 1 KB of LDS in lane order),
 // in the swizzled chunk layout of lds_layout.h, and read back as MFMA operands
 // with one of two fixed lane patterns whose per-lane offsets are computed once.
 #pragma once
