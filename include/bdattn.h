@@ -144,8 +144,22 @@ int64_t bdattn_cad_split(const int32_t *cu_seqlens, int32_t n_docs, int64_t max_
 
 void bdattn_plan_destroy(bdattn_plan *plan);
 
-/* Size (bytes) of the per-call workspace: the plan's tables, uploaded by each call. */
+/* Size (bytes) of the per-call workspace: the plan's tables, uploaded by each call,
+ * and, when the plan splits its dK/dV key tiles, the fp32 dK/dV partials. */
 int64_t bdattn_plan_workspace_bytes(const bdattn_plan *plan);
+
+/* Workgroups per key tile of the dK/dV kernel (a schedule choice; results do not
+ * depend on it beyond fp32 rounding order, and are deterministic for each value).
+ * With one, each workgroup walks every query tile that attends its 128 keys and
+ * writes dK/dV directly.  A problem with few key tiles would leave most compute
+ * units idle that way, so a plan splits each walk over `split` workgroups that
+ * write fp32 partials into the workspace, summed in a fixed order by a reduction
+ * kernel.  plan_create picks the split automatically (0); this call overrides it
+ * (0 = automatic, 1..8 = fixed) and must come before the plan's first use
+ * (BDATTN_EINVAL otherwise, and for values outside 0..8).  It changes the
+ * workspace size.  bdattn_plan_dkdv_split returns the value in force. */
+int bdattn_plan_set_dkdv_split(bdattn_plan *plan, int32_t split);
+int32_t bdattn_plan_dkdv_split(const bdattn_plan *plan);
 /* Legal (query, key) pairs per query head: the useful-work count. */
 int64_t bdattn_plan_useful_pairs(const bdattn_plan *plan);
 /* Query rows, and key rows of the clean (or packed) range and of the local corrupted K/V. */

@@ -50,6 +50,8 @@ _SIGS = {
     "bdattn_plan_destroy": (None, [c_void_p]),
     "bdattn_plan_workspace_bytes": (c_int64, [c_void_p]),
     "bdattn_plan_useful_pairs": (c_int64, [c_void_p]),
+    "bdattn_plan_set_dkdv_split": (c_int32, [c_void_p, c_int32]),
+    "bdattn_plan_dkdv_split": (c_int32, [c_void_p]),
     "bdattn_plan_n_q": (c_int64, [c_void_p]),
     "bdattn_plan_n_kv": (c_int64, [c_void_p, c_int32]),
     "bdattn_plan_export": (c_int64, [c_void_p, c_int32, c_void_p, c_int64]),
@@ -170,6 +172,14 @@ class Plan:
     @property
     def useful_pairs(self) -> int:
         return lib().bdattn_plan_useful_pairs(self._h)
+
+    @property
+    def dkdv_split(self) -> int:
+        return lib().bdattn_plan_dkdv_split(self._h)
+
+    def set_dkdv_split(self, split: int):
+        """0 = automatic, 1..8 = dK/dV workgroups per key tile (before first use)."""
+        _check(lib().bdattn_plan_set_dkdv_split(self._h, split))
 
     @property
     def n_q(self) -> int:

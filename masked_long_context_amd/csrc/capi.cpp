@@ -193,6 +193,9 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   a.group = p.h_q / p.h_kv;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.split = p.dkdv_split;
+  for (int seg = 0; seg < 2; ++seg)
+    a.part[seg] = p.dkdv_split > 1 ? reinterpret_cast<float *>((char *)ws + p.off_part[seg]) : nullptr;
   HIP_CHECK(bdattn::launch_bwd(a, p.d, s, do_dkdv, do_dq), "backward kernels");
   return BDATTN_OK;
 }
@@ -291,6 +294,18 @@ void bdattn_plan_destroy(bdattn_plan *pl) {
 int64_t bdattn_plan_workspace_bytes(const bdattn_plan *pl) { return pl ? pl->p.ws_bytes : BDATTN_EINVAL; }
 int64_t bdattn_plan_useful_pairs(const bdattn_plan *pl) { return pl ? pl->p.useful_pairs : BDATTN_EINVAL; }
 int64_t bdattn_plan_n_q(const bdattn_plan *pl) { return pl ? pl->p.n_q : BDATTN_EINVAL; }
+int bdattn_plan_set_dkdv_split(bdattn_plan *pl, int32_t split) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  if (split < 0 || split > BDATTN_MAX_SPLIT)
+    return fail(BDATTN_EINVAL, "split must be 0 (automatic) or 1.." + std::to_string(BDATTN_MAX_SPLIT));
+  std::lock_guard<std::mutex> lk(pl->mu);
+  if (pl->p.used) return fail(BDATTN_EINVAL, "the plan has already been used");
+  bdattn::set_dkdv_split(pl->p, split);
+  return BDATTN_OK;
+}
+
+int32_t bdattn_plan_dkdv_split(const bdattn_plan *pl) { return pl ? pl->p.dkdv_split : BDATTN_EINVAL; }
+
 int64_t bdattn_plan_n_kv(const bdattn_plan *pl, int32_t seg) {
   if (!pl || seg < 0 || seg > 1) return fail(BDATTN_EINVAL, "bad plan or segment");
   return pl->p.n_seg[seg];

@@ -66,8 +66,8 @@ struct DkdvLds {
 // The roles share no data inside an iteration, so one barrier per iteration
 // suffices.
 template <int D, int KT, int ROLE>
-__device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int lb, int le, int kvh,
-                                          int wave, int lane, const DkdvLds<D> &L) {
+__device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int lb, int t0, int nt, int chunk,
+                                          int kvh, int wave, int lane, const DkdvLds<D> &L) {
   constexpr int BM = BDATTN_BWD_BM;
   constexpr int NWR = 4 / KT;   // waves per role
   constexpr int NC = D / 16, ND = D / 32;
@@ -101,7 +101,9 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   const int pofs = kw * (2 * KT * 4 * 64);   // this wave pair's slot in a P buffer
   auto pidx = [&](int h2, int kt, int s4) { return pofs + ((h2 * KT + kt) * 4 + s4) * 64 + lane; };
 
-  const int n = (le - lb) * G;          // tiles: list entry lb + t / G, head kvh * G + t % G
+  // This workgroup's tiles t = 0 .. n - 1 are the key tile's tiles t0 + t: list
+  // entry lb + (t0 + t) / G, head kvh * G + (t0 + t) % G.
+  const int n = nt;
   const int q_stride = a.h_q * D;
   // Tile t's list entry record {q0, rows, full, q-tile} (a scalar load; t is
   // clamped to n - 1, so the entry stays inside this key tile's list).  Records
@@ -109,13 +111,13 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   // scalar load's latency.
   struct TileRef { int q0, nrows, full, h; };
   const u32x4 *lrec = reinterpret_cast<const u32x4 *>(a.lrec);
-  auto fetch = [&](int t) { return ld_table(lrec, lb + min(t, n - 1) / G); };
+  auto fetch = [&](int t) { return ld_table(lrec, lb + (t0 + min(t, n - 1)) / G); };
   auto ref = [&](const u32x4 &r, int t) {
     TileRef x;
     x.q0 = (int)r[0];
     x.nrows = (int)r[1];
     x.full = (int)r[2];
-    x.h = kvh * G + min(t, n - 1) % G;
+    x.h = kvh * G + (t0 + min(t, n - 1)) % G;
     return x;
   };
   u32x4 rec1 = {0u, 0u, 0u, 0u}, rec2 = {0u, 0u, 0u, 0u};   // records of tiles i + 1 and i + 2
@@ -357,6 +359,26 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   }
 
   const float mul = ROLE == 0 ? 1.f : a.scale;
+  if (a.split > 1) {
+    // fp32 partial of this workgroup's share of the walk: dK at ro = 0, dV at 1
+    const int ro = ROLE == 0 ? 1 : 0;
+    const int64_t n_s = a.n_seg[s];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      if (!kvalid[kt]) continue;
+      float *outp = a.part[s] + ((((int64_t)ro * a.split + chunk) * n_s + key[kt]) * a.h_kv + kvh) * D;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[dt][kt][4 * s4 + i] * mul;
+          *reinterpret_cast<f32x4 *>(outp + 32 * dt + 8 * s4 + 4 * g) = v;
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     if (!kvalid[kt]) continue;
@@ -397,11 +419,34 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ f32x4 pb1[4 * 2 * 4 * 64];
   const DkdvLds<D> L = {{qs0, qs1, qs2}, {ds0, ds1}, {sq0, sq1, sq2}, {sd0, sd1}, {pb0, pb1}};
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int kti = blockIdx.x / a.h_kv, kvh = blockIdx.x % a.h_kv;
+  // workgroup = (key tile, share of its walk, KV head); consecutive workgroups
+  // take different KV heads, so each XCD keeps to one KV head
+  const int kvh = blockIdx.x % a.h_kv, rest = blockIdx.x / a.h_kv;
+  const int kti = rest / a.split, chunk = rest % a.split;
   const int s = ld_table(a.ktiles, (int64_t)kti * 4), k0 = ld_table(a.ktiles, (int64_t)kti * 4 + 1);
   const int lb = ld_table(a.ktiles, (int64_t)kti * 4 + 2), le = ld_table(a.ktiles, (int64_t)kti * 4 + 3);
-  if (wave < 4 / kDkdvKT) dkdv_role<D, kDkdvKT, 0>(a, s, k0, lb, le, kvh, wave, lane, L);
-  else dkdv_role<D, kDkdvKT, 1>(a, s, k0, lb, le, kvh, wave, lane, L);
+  const int total = (le - lb) * a.group;
+  const int t0 = (int)((int64_t)total * chunk / a.split), t1 = (int)((int64_t)total * (chunk + 1) / a.split);
+  if (wave < 4 / kDkdvKT) dkdv_role<D, kDkdvKT, 0>(a, s, k0, lb, t0, t1 - t0, chunk, kvh, wave, lane, L);
+  else dkdv_role<D, kDkdvKT, 1>(a, s, k0, lb, t0, t1 - t0, chunk, kvh, wave, lane, L);
+}
+
+// Sum of the split dK/dV partials of one key segment, in chunk order (so the
+// result does not depend on scheduling), to bf16: n4 groups of 4 elements per
+// tensor, dK groups first, then dV.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float *part, int split, int64_t n4, bf16 *dk,
+                                                          bf16 *dv) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const int ro = i >= n4 ? 1 : 0;
+  const int64_t e = i - ro * n4;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(part) + (int64_t)ro * split * n4 + e;
+  f32x4 acc = src[0];
+  for (int c = 1; c < split; ++c) acc += src[(int64_t)c * n4];
+  bf16x4 b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b[k] = (bf16)acc[k];
+  reinterpret_cast<bf16x4 *>(ro ? dv : dk)[e] = b;
 }
 
 template <int D>
@@ -556,12 +601,22 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void d
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, bool dq) {
-  const int64_t kblocks = dkdv ? (int64_t)a.n_kt * a.h_kv : 0;
+  const int64_t kblocks = dkdv ? (int64_t)a.n_kt * a.h_kv * a.split : 0;
   if (kblocks > 0) {
     if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)kblocks), dim3(kDkdvThreads), 0, s, a);
     else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)kblocks), dim3(kDkdvThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.split > 1) {
+      for (int seg = 0; seg < 2; ++seg) {
+        const int64_t n4 = (int64_t)a.n_seg[seg] * a.h_kv * d / 4;
+        if (n4 == 0) continue;
+        hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, s,
+                           (const float *)a.part[seg], a.split, n4, (bf16 *)a.dk[seg], (bf16 *)a.dv[seg]);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
   }
   const int64_t qblocks = dq ? (int64_t)a.n_items * a.h_q : 0;
   if (qblocks > 0) {

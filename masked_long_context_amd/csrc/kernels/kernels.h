@@ -33,6 +33,10 @@ struct BwdArgs {
   const int32_t *lrec;      // [n_list][4] per list entry {q0, rows, full, q-tile}
   int32_t n_items, n_kt, n_bq, n_q, h_q, h_kv, group;
   float scale, scale_log2;
+  // dK/dV workgroups per key tile; above 1 each writes fp32 partials to
+  // part[s] ([2][split][n_seg][h_kv][d], dK then dV) and a reduction sums them
+  int32_t split;
+  float *part[2];
 };
 
 struct PrepArgs {

@@ -160,7 +160,7 @@ void finish(Plan &p) {
   if (!p.list.empty()) std::memcpy(p.image.data() + h.off_list, p.list.data(), p.list.size() * 4);
   if (!p.lrec.empty()) std::memcpy(p.image.data() + h.off_lrec, p.lrec.data(), p.lrec.size() * 4);
 
-  p.ws_bytes = h.image_bytes;
+  set_dkdv_split(p, 0);
   p.id = g_next_id.fetch_add(1);
 }
 
@@ -172,6 +172,37 @@ std::string check_heads(int32_t h_q, int32_t h_kv, int32_t d) {
 }
 
 }  // namespace
+
+// Splitting a key tile's walk over several workgroups only pays when the
+// kernel would otherwise leave compute units idle: small problems have few key
+// tiles, each with a long query-tile list, so one workgroup per key tile puts
+// the whole list on one compute unit.
+void set_dkdv_split(Plan &p, int32_t split) {
+  const int64_t n_wg = (int64_t)p.kt.size() * p.h_kv;
+  // bytes of one split's dK and dV partials over both key segments
+  const int64_t part = 2 * (p.n_seg[0] + p.n_seg[1]) * p.h_kv * (int64_t)p.d * 4;
+  if (split == 0) {
+    int64_t longest = 0;
+    for (const KTile &k : p.kt) longest = std::max<int64_t>(longest, (int64_t)(k.end - k.begin) * (p.h_q / p.h_kv));
+    int64_t f = 1;
+    if (n_wg > 0 && n_wg < BDATTN_SPLIT_TARGET / 2) {
+      f = std::min<int64_t>(BDATTN_MAX_SPLIT, (BDATTN_SPLIT_TARGET + n_wg - 1) / n_wg);
+      f = std::min<int64_t>(f, longest / BDATTN_SPLIT_MIN_ITERS);
+      while (f > 1 && f * part > BDATTN_SPLIT_MAX_BYTES) --f;
+    }
+    split = (int32_t)std::max<int64_t>(1, f);
+  }
+  p.dkdv_split = split;
+  int64_t off = p.hdr.image_bytes;
+  p.off_part[0] = p.off_part[1] = 0;
+  if (split > 1) {
+    for (int s = 0; s < 2; ++s) {
+      p.off_part[s] = off;
+      off = align_up(off + 2 * (int64_t)split * p.n_seg[s] * p.h_kv * p.d * 4, BDATTN_ALIGN);
+    }
+  }
+  p.ws_bytes = off;
+}
 
 std::string build_bdlm(Plan &p, int64_t L, int32_t B, int64_t q_off, int64_t q_len,
                        const int64_t *owned, int64_t n_owned, int64_t kv_off, int64_t kv_len,

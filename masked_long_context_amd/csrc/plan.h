@@ -43,8 +43,11 @@ struct Plan {
   // Device image of the tables (uploaded into the head of each workspace).
   std::vector<uint8_t> image;
   ImageHeader hdr{};
-  // Workspace = the uploaded tables.
+  // Workspace = the uploaded tables, then (when the dK/dV key tiles are split)
+  // the fp32 dK/dV partials of each key segment: [2][split][n_seg][h_kv][d].
   int64_t ws_bytes = 0;
+  int32_t dkdv_split = 1;       // workgroups per key tile in the dK/dV kernel
+  int64_t off_part[2] = {0, 0};
   // Pinned copy of `image` for asynchronous uploads (made on first use).
   void *pinned = nullptr;
   bool used = false;
@@ -65,5 +68,9 @@ int64_t cad_split(const int32_t *cu, int32_t n_docs, int64_t max_pairs, int32_t 
                   int32_t *kv_src, int64_t cap, int64_t *total_ctx);
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Sets the dK/dV split factor (0: automatic, else 1 .. BDATTN_MAX_SPLIT) and the
+// workspace layout that follows from it.
+void set_dkdv_split(Plan &p, int32_t split);
 
 }  // namespace bdattn

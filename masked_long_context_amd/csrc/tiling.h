@@ -12,6 +12,16 @@
 #define BDATTN_BWD_WAVES 4
 #define BDATTN_BWD_BM 64
 #define BDATTN_BWD_BN 128
+// A plan whose dK/dV kernel would occupy few workgroups splits every key tile's
+// query-tile walk over up to BDATTN_MAX_SPLIT workgroups, each writing fp32
+// partial dK/dV that a reduction kernel sums in a fixed order.  Automatic
+// splitting aims at BDATTN_SPLIT_TARGET workgroups, keeps at least
+// BDATTN_SPLIT_MIN_ITERS query tiles per workgroup, and keeps the partials
+// within BDATTN_SPLIT_MAX_BYTES.
+#define BDATTN_MAX_SPLIT 8
+#define BDATTN_SPLIT_TARGET 1024
+#define BDATTN_SPLIT_MIN_ITERS 8
+#define BDATTN_SPLIT_MAX_BYTES (512LL << 20)
 // Alignment of every buffer carved out of a workspace.
 #define BDATTN_ALIGN 256
 

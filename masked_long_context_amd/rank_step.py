@@ -30,11 +30,14 @@ from . import bdattn as B
 
 class BdlmRankStep:
     def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda",
-                 part_dtype=torch.float32):
+                 part_dtype=torch.float32, dkdv_split: int = 0):
         self.problem = problem
         self.shards = list(shards)
         self.device = device
         self.plans: List[B.Plan] = [B.Plan.from_problem(problem.with_kv(o, n, loc)) for (o, n, loc) in shards]
+        if dkdv_split:   # 0 keeps each plan's automatic choice
+            for pl in self.plans:
+                pl.set_dkdv_split(dkdv_split)
         self.active = [i for i, pl in enumerate(self.plans) if pl.useful_pairs > 0]
         p = problem
         self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim

@@ -86,9 +86,9 @@ def poison_(*ts):
             t.fill_(float("nan"))
 
 
-def run_gpu_bdlm(cfg: wl.BdlmConfig, inp, shards=None, poison=True) -> dict:
+def run_gpu_bdlm(cfg: wl.BdlmConfig, inp, shards=None, poison=True, dkdv_split=0) -> dict:
     g = {k: v.to("cuda") for k, v in inp.items()}
-    step = BdlmRankStep(cfg.problem, shards if shards is not None else cfg.shards)
+    step = BdlmRankStep(cfg.problem, shards if shards is not None else cfg.shards, dkdv_split=dkdv_split)
     if poison:
         poison_(step.o_parts, step.lse_parts, step.o, step.lse, step.delta, step.dq_acc, step.dq,
                 step.dk_clean, step.dv_clean, step.dk_corr, step.dv_corr)

@@ -202,3 +202,31 @@ def test_plan_sizes_and_counts():
     # clean rows at positions 64..127 (blocks 2, 3) see keys [0, 96) and [0, 128) of the range;
     # block 3 sees [0, 96) plus its own 32; block 1 sees [0, 32) plus its own 32
     assert plan.useful_pairs == 32 * 96 + 32 * 128 + 32 * (96 + 32) + 32 * (32 + 32)
+
+
+def test_dkdv_split_choice_and_override():
+    """The automatic dK/dV split leaves a problem with many key tiles unsplit and
+    splits a small one; an override is validated, resizes the workspace for the
+    fp32 partials ([2][split][n_seg][h_kv][d] per segment), and 1 removes them."""
+    # one clean K/V range of 16384 keys, 8 KV heads: 128 key tiles x 8 heads = 1024 workgroups
+    big = B.Plan.bdlm(clean_len=262144, block_size=32, q_clean_offset=131072, q_clean_len=16384,
+                      owned_blocks=list(range(2048, 2304)), kv_clean_offset=0, kv_clean_len=16384,
+                      with_local_corrupt=False, h_q=32, h_kv=8, head_dim=128)
+    assert big.dkdv_split == 1
+    small = B.Plan.bdlm(**_problem())
+    base = small.workspace_bytes
+    for bad in (-1, 9, 100):
+        with pytest.raises(B.BdattnError) as e:
+            small.set_dkdv_split(bad)
+        assert e.value.status == B.EINVAL
+    small.set_dkdv_split(1)
+    assert small.dkdv_split == 1
+    unsplit = small.workspace_bytes
+    small.set_dkdv_split(4)
+    assert small.dkdv_split == 4
+    keys = small.n_kv(0) + small.n_kv(1)
+    assert small.workspace_bytes >= unsplit + 2 * 4 * keys * 2 * 128 * 4   # dK+dV, split 4, h_kv 2, d 128, fp32
+    small.set_dkdv_split(1)
+    assert small.workspace_bytes == unsplit
+    small.set_dkdv_split(0)
+    assert small.workspace_bytes == base

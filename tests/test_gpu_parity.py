@@ -78,6 +78,25 @@ def test_small_rank_shares(spec):
     compare_bdlm(fused, want, cfg.name + " fused whole range")
 
 
+@pytest.mark.parametrize("spec,split", [((2048, 32, 8, 5, 8, 2, 128, 8), 1), ((2048, 32, 8, 5, 8, 2, 128, 8), 3),
+                                        ((1024, 128, 2, 1, 2, 1, 128, 2), 8), ((768, 16, 2, 1, 16, 2, 64, 3), 5)],
+                         ids=["L2048_split1", "L2048_split3", "L1024_B128_split8", "L768_d64_split5"])
+def test_dkdv_split_factors(spec, split):
+    """dK/dV with each key tile's query-tile walk split over `split` workgroups
+    (fp32 partials summed in a fixed order), and unsplit (1): equal to the oracle,
+    and bit-for-bit equal across two runs."""
+    L, Bs, R, rank, hq, hkv, d, ns = spec
+    cfg = wl.small_bdlm_config(L, Bs, R, rank, hq, hkv, d, ns)
+    inp = wl.bdlm_inputs(cfg, seed=3)
+    want = oracle_bdlm_full(cfg, inp)
+    a = run_gpu_bdlm(cfg, inp, dkdv_split=split)
+    assert all(pl.dkdv_split == split for pl in a["step"].plans)
+    compare_bdlm(a, want, f"{cfg.name} split {split}")
+    b = run_gpu_bdlm(cfg, inp, dkdv_split=split)
+    for k in ("dk_clean", "dv_clean", "dk_corr", "dv_corr"):
+        assert torch.equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("spec", [(512, 16, 4, 3, 4, 2, 128, 4), (768, 32, 2, 0, 2, 1, 64, 3),
                                   (1600, 200, 4, 2, 2, 2, 64, 4)],
                          ids=lambda s: "L{}_B{}_R{}_r{}_h{}x{}_d{}_s{}".format(*s))
