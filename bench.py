@@ -336,6 +336,11 @@ def main():
     dk = per["dkdv"]
     dk_flops_per_launch = pairs * p.h_q * 8 * p.head_dim / n_sh
     dk_achieved = dk_flops_per_launch / (dk["ms_per_launch"] * 1e-3) / 1e12
+    # algorithmic HBM bytes of one dK/dV launch, averaged over the launches: Q and dO
+    # of every query row, the range's K and V read and dK and dV written, LSE and delta
+    kv_rows = sum(n + (p.n_corr if loc else 0) for (_, n, loc) in shards) / n_sh
+    dk_alg_bytes = int(2 * p.n_q * p.h_q * p.head_dim * 2 + 4 * kv_rows * p.h_kv * p.head_dim * 2
+                       + 2 * p.h_q * p.n_q * 4)
     merge_ms, merge_n = tot.get("merge", (0.0, 1))
     merge_bytes = p.n_q * p.h_q * (n_act * (4 * p.head_dim + 4) + (2 * p.head_dim + 4))
     merge_gbs = merge_bytes / (merge_ms / merge_n * 1e-3) / 1e9 if merge_ms else 0.0
@@ -364,7 +369,8 @@ def main():
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": f"dkdv_kernel<{p.head_dim}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": profiled_traffic(workload), "ms_per_launch": round(dk["ms_per_launch"], 4),
+                     "traffic": profiled_traffic(workload), "algorithmic_bytes": dk_alg_bytes,
+                     "ms_per_launch": round(dk["ms_per_launch"], 4),
                      "flops_per_launch": dk_flops_per_launch},
         # MFMA work the kernels execute per useful pair and q-head: 4d forward, 8d dK/dV,
         # 6d dQ (S and dP recomputed); 14d of it is counted in `value`
@@ -381,6 +387,7 @@ def main():
     }
     if ceiling is not None:
         ceiling["dominant_kernel_frac"] = round(dk_achieved / ceiling["tflops"], 4)
+        ceiling["kernel_fracs"] = {k: round(v["tflops"] / ceiling["tflops"], 4) for k, v in per.items()}
         ceiling["step_executed_frac"] = round(out["executed_tflops"] / ceiling["tflops"], 4)
         out["roofline"]["sustained_ceiling"] = ceiling
     if args.config in (3, 7):
