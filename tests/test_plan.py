@@ -236,3 +236,24 @@ def test_cad_split_reproduces_document_causal_attention():
         if cu[-1]:
             tp = B.Plan.tasks(q_cu, k_cu, True, 2, 1, 64).useful_pairs
             assert tp == B.Plan.varlen(cu, True, 2, 1, 64).useful_pairs == int(mv.sum())
+
+
+def test_dkdv_split_follows_the_occupancy_rule():
+    """Automatic dK/dV split: F = min(8, ceil(1024 / workgroups), longest walk / 8),
+    and 1 when the plan already has 512 or more workgroups (key tiles x KV heads)."""
+    from masked_long_context_amd import bdattn as B
+    from masked_long_context_amd import workloads as wl
+    cfg2 = wl.config(2)
+    got = []
+    for sh in cfg2.shards:
+        pl = B.Plan.from_problem(cfg2.problem.with_kv(*sh))
+        kt = pl.export(3)
+        n_wg = len(kt) * cfg2.problem.h_kv
+        longest = int((kt[:, 3] - kt[:, 2]).max()) * (cfg2.problem.h_q // cfg2.problem.h_kv)
+        want = 1 if n_wg >= 512 else max(1, min(8, -(-1024 // n_wg), longest // 8))
+        assert pl.dkdv_split == want, (sh, pl.dkdv_split, want)
+        got.append(pl.dkdv_split)
+    assert got[0] == 7 and all(f == 8 for f in got[1:]), got
+    cfg3 = wl.config(3)
+    for sh in list(cfg3.shards)[:3]:
+        assert B.Plan.from_problem(cfg3.problem.with_kv(*sh)).dkdv_split == 1
