@@ -272,6 +272,9 @@ def main():
                     help="workloads 1-3, 5: pass the whole clean K/V as one range (all shards resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step as a HIP graph and time its replays (launch-bound small "
+                         "workloads); value is then the replay rate, the eager figures stay beside it")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the sustained-MFMA ceiling measurement (vendor bf16 GEMM, about 1 s)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -353,6 +356,24 @@ def main():
         torch.cuda.synchronize()
         print(f"# bench: copy calibration moved {src.numel() * 4} bytes each way", file=sys.stderr, flush=True)
 
+    graph = None
+    if args.graph:
+        from masked_long_context_amd.rank_step import StepGraph
+        sg = StepGraph(step, *args_)
+        for _ in range(args.warmup):
+            sg.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            sg.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        graph = {"eager_value": round(tflops, 2), "eager_ms_per_step": round(ms, 4)}
+        ms, tflops = gms, flops / (gms * 1e-3) / 1e12
+        del sg
+
     ceiling = None
     if not args.no_ceiling:
         try:
@@ -363,6 +384,8 @@ def main():
     metric = METRIC if args.config == 3 else f"BDLM attention fwd+bwd useful-pair TFLOP/s and % bf16 MFMA peak, {cfg.name}"
     if args.fused:
         metric += " (all clean K/V resident, one fused range)"
+    if args.graph:
+        metric += " (step replayed from a HIP graph)"
     out = {
         "metric": metric, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
@@ -390,6 +413,9 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    if graph is not None:
+        out["config"]["hip_graph"] = True
+        out["graph"] = graph
     if ceiling is not None:
         ceiling["dominant_kernel_frac"] = round(dk_achieved / ceiling["tflops"], 4)
         ceiling["kernel_fracs"] = {k: round(v["tflops"] / ceiling["tflops"], 4) for k, v in per.items()}

@@ -113,6 +113,33 @@ class BdlmRankStep:
         return self.backward(q, k_clean, v_clean, k_corr, v_corr, dout)
 
 
+class StepGraph:
+    """A step (BdlmRankStep, VarlenStep or TaskStep) captured once as a HIP graph
+    (torch.cuda.CUDAGraph over torch's current stream, which the library launches
+    on) and replayed.  The graph holds every table upload and kernel launch of one
+    step, so a replay costs one graph launch where the eager step issues one call
+    per kernel; this matters when the step is launch-bound (small problems).  The
+    input and output tensors are fixed at capture: refill the inputs in place.
+    The step runs once eagerly first, so that the plans' pinned table copies exist
+    before capture (no host allocation happens during it)."""
+
+    def __init__(self, step, *inputs):
+        import torch
+        self.step, self.inputs = step, inputs
+        timer, step.timer = step.timer, None
+        step.step(*inputs)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.outputs = step.step(*inputs)
+        torch.cuda.synchronize()
+        step.timer = timer
+
+    def replay(self):
+        self.graph.replay()
+        return self.outputs
+
+
 class VarlenStep:
     """Forward + backward of packed independent shards (one call each)."""
 

@@ -244,3 +244,30 @@ def test_repeat_runs_are_bitwise_stable(cfg2_data):
     for k in ("o", "lse", "dk_clean", "dv_clean", "dk_corr", "dv_corr"):
         assert torch.equal(a[k], b[k]), k
     check_close("dq run-to-run", a["dq"], to64(b["dq"]), max_abs=1e-2, rel=1e-3)
+
+
+def test_rank_step_replayed_from_a_hip_graph():
+    """The whole rank step captured as a HIP graph: three replays, each after its
+    outputs were poisoned and another step ran eagerly in between, reproduce the
+    eager step bit for bit (and so the oracle)."""
+    from masked_long_context_amd.rank_step import BdlmRankStep, StepGraph
+    cfg = wl.small_bdlm_config(1024, 32, 4, 2, 8, 1, 128, 4)
+    inp = wl.bdlm_inputs(cfg, seed=5)
+    g = {k: v.to("cuda") for k, v in inp.items()}
+    args = (g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+    names = ("o", "lse", "dq", "dk_clean", "dv_clean", "dk_corr", "dv_corr")
+    eager = BdlmRankStep(cfg.problem, cfg.shards)
+    eager.step(*args)
+    torch.cuda.synchronize()
+    want = {n: getattr(eager, n).clone() for n in names}
+    compare_bdlm(dict(want), oracle_bdlm_full(cfg, inp), cfg.name + " eager")
+    step = BdlmRankStep(cfg.problem, cfg.shards)
+    sg = StepGraph(step, *args)
+    for r in range(3):
+        poison_(*(getattr(step, n) for n in names), step.dq_acc, step.delta)
+        eager.step(*args)                 # eager work on the same stream between replays
+        torch.cuda.synchronize()
+        sg.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(step, n), want[n]), (r, n)
