@@ -272,6 +272,8 @@ def main():
                     help="workloads 1-3, 5: pass the whole clean K/V as one range (all shards resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--streams", type=int, default=1,
+                    help="spread the independent per-shard calls over this many streams (workloads 1-3, 5, 7)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step as a HIP graph and time its replays (launch-bound small "
                          "workloads); value is then the replay rate, the eager figures stay beside it")
@@ -302,7 +304,7 @@ def main():
     # backward kernel runs once over the whole range
     shards = [(0, p.clean_len, True)] if args.fused else list(cfg.shards)
     workload = cfg.name + ("_fused_whole_range" if args.fused else "")
-    step = BdlmRankStep(p, shards)
+    step = BdlmRankStep(p, shards, streams=args.streams)
     timer = EventTimer()
     step.timer = timer
     pairs = step.useful_pairs
@@ -413,6 +415,8 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    if args.streams > 1:
+        out["config"]["streams"] = args.streams
     if graph is not None:
         out["config"]["hip_graph"] = True
         out["graph"] = graph

@@ -30,7 +30,7 @@ from . import bdattn as B
 
 class BdlmRankStep:
     def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda",
-                 part_dtype=torch.float32, dkdv_split: int = 0):
+                 part_dtype=torch.float32, dkdv_split: int = 0, streams: int = 1):
         self.problem = problem
         self.shards = list(shards)
         self.device = device
@@ -41,7 +41,14 @@ class BdlmRankStep:
         self.active = [i for i, pl in enumerate(self.plans) if pl.useful_pairs > 0]
         p = problem
         self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
-        self.ws = B.workspace(max(pl.workspace_bytes for pl in self.plans), device)
+        ws_bytes = max(pl.workspace_bytes for pl in self.plans)
+        self.ws = B.workspace(ws_bytes, device)
+        # streams > 1: the per-shard forward and dK/dV calls, which are independent,
+        # alternate over the caller's stream and streams - 1 side streams (default
+        # priority), each with its own workspace; the dQ calls, which add into one
+        # accumulator, stay on the caller's stream in shard order
+        self.side = [torch.cuda.Stream(device=device) for _ in range(max(1, int(streams)) - 1)]
+        self.ws_side = [B.workspace(ws_bytes, device) for _ in self.side]
         # one active shard: its forward writes O and LSE itself (no partials)
         self.direct = len(self.active) == 1
         n_parts = 0 if self.direct else max(1, len(self.active))
@@ -67,6 +74,25 @@ class BdlmRankStep:
         import contextlib
         return self.timer(tag) if self.timer is not None else contextlib.nullcontext()
 
+    def _lane(self, j):
+        """Stream context and workspace of the j-th independent call (lane 0: the
+        caller's stream)."""
+        import contextlib
+        k = j % (len(self.side) + 1)
+        if k == 0:
+            return contextlib.nullcontext(), self.ws
+        return torch.cuda.stream(self.side[k - 1]), self.ws_side[k - 1]
+
+    def _fork(self):
+        main = torch.cuda.current_stream()
+        for s in self.side:
+            s.wait_stream(main)
+
+    def _join(self):
+        main = torch.cuda.current_stream()
+        for s in self.side:
+            main.wait_stream(s)
+
     def forward(self, q, k_clean, v_clean, k_corr, v_corr):
         if not self.active:
             self.o.zero_()
@@ -79,12 +105,15 @@ class BdlmRankStep:
                 B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
                              k_corr if local else None, v_corr if local else None, self.o, self.lse, self.ws)
             return self.o, self.lse
+        self._fork()
         for slot, i in enumerate(self.active):
             off, n, local = self.shards[i]
-            with self._t("fwd"):
+            lane, ws = self._lane(slot)
+            with lane, self._t("fwd"):
                 B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
                              k_corr if local else None, v_corr if local else None,
-                             self.o_parts[slot], self.lse_parts[slot], self.ws)
+                             self.o_parts[slot], self.lse_parts[slot], ws)
+        self._join()
         with self._t("merge"):
             B.bdattn_lse_merge(self.o_parts[:len(self.active)], self.lse_parts[:len(self.active)],
                                self.o, self.lse)
@@ -94,16 +123,19 @@ class BdlmRankStep:
         with self._t("prepare"):
             B.bdattn_bwd_prepare(self.plans[0], self.o, dout, self.delta, self.dq_acc)
         # the two steps of bdattn_bwd, called apart so that each can be timed
+        self._fork()
         for i, (off, n, local) in enumerate(self.shards):
             kc, vc = k_clean[off:off + n], v_clean[off:off + n]
             kx, vx = (k_corr, v_corr) if local else (None, None)
-            with self._t("dkdv"):
+            lane, ws = self._lane(i)
+            with lane, self._t("dkdv"):
                 B.bdattn_bwd_dkdv(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta,
                                   self.dk_clean[off:off + n], self.dv_clean[off:off + n],
-                                  self.dk_corr if local else None, self.dv_corr if local else None, self.ws)
+                                  self.dk_corr if local else None, self.dv_corr if local else None, ws)
             with self._t("dq"):
                 B.bdattn_bwd_dq(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta, self.dq_acc,
                                 self.ws)
+        self._join()
         with self._t("finalize"):
             B.bdattn_dq_finalize(self.dq_acc, self.dq)
         return self.dq, self.dk_clean, self.dv_clean, self.dk_corr, self.dv_corr

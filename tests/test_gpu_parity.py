@@ -271,3 +271,35 @@ def test_rank_step_replayed_from_a_hip_graph():
         torch.cuda.synchronize()
         for n in names:
             assert torch.equal(getattr(step, n), want[n]), (r, n)
+
+
+@pytest.mark.parametrize("streams", [2, 3])
+def test_rank_step_on_several_streams(streams):
+    """Shard calls spread over several streams (the dQ calls kept in order on the
+    caller's stream): the same bits as one stream, eagerly and replayed from a
+    HIP graph captured across the streams."""
+    from masked_long_context_amd.rank_step import BdlmRankStep, StepGraph
+    cfg = wl.small_bdlm_config(2048, 32, 8, 5, 8, 2, 128, 8)
+    inp = wl.bdlm_inputs(cfg, seed=6)
+    g = {k: v.to("cuda") for k, v in inp.items()}
+    args = (g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+    names = ("o", "lse", "dq", "dk_clean", "dv_clean", "dk_corr", "dv_corr")
+    one = BdlmRankStep(cfg.problem, cfg.shards)
+    one.step(*args)
+    torch.cuda.synchronize()
+    want = {n: getattr(one, n).clone() for n in names}
+    multi = BdlmRankStep(cfg.problem, cfg.shards, streams=streams)
+    poison_(*(getattr(multi, n) for n in names))
+    multi.step(*args)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(getattr(multi, n), want[n]), ("eager", n)
+    sg = StepGraph(multi, *args)
+    for r in range(2):
+        poison_(*(getattr(multi, n) for n in names), multi.dq_acc)
+        one.step(*args)
+        torch.cuda.synchronize()
+        sg.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(multi, n), want[n]), ("replay", r, n)
