@@ -216,6 +216,23 @@ def bench_varlen(args, cfg):
     ms = start.elapsed_time(end) / args.steps
     tot = timer.totals_ms()
     tflops = flops / (ms * 1e-3) / 1e12
+    graph = None
+    if args.graph:
+        from masked_long_context_amd.rank_step import StepGraph
+        sg = StepGraph(step, *a)
+        for _ in range(args.warmup):
+            sg.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            sg.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph = {"eager_value": round(tflops, 2), "eager_ms_per_step": round(ms, 4)}
+        ms = g0.elapsed_time(g1) / args.steps
+        tflops = flops / (ms * 1e-3) / 1e12
+        del sg
     fwd_ms = tot["fwd"][0] / args.steps
     bwd_ms = tot["bwd"][0] / args.steps
     out = {
@@ -234,6 +251,10 @@ def bench_varlen(args, cfg):
                     "prepare_ms": round(tot["prepare"][0] / args.steps, 4),
                     "finalize_ms": round(tot["finalize"][0] / args.steps, 4)},
     }
+    if graph is not None:
+        out["metric"] += " (step replayed from a HIP graph)"
+        out["config"]["hip_graph"] = True
+        out["graph"] = graph
     print(json.dumps(out), flush=True)
 
 
