@@ -3,7 +3,8 @@
 The rank holds its clean query rows, the corrupted blocks it owns and their
 local corrupted K/V, and sees the clean K/V as position shards ("Block
 Parallelism For Efficient Distributed Long-Context Diffusion Language Model
-Training", English abstract).  The step runs, on one HIP stream:
+Training", English abstract).  The step runs, on the caller's HIP stream (or,
+optionally, with its independent per-shard calls spread over several streams):
 
     for each clean K/V shard s:  bdattn_fwd  -> partial (O_s, LSE_s)
     bdattn_lse_merge             -> O, LSE
@@ -16,7 +17,9 @@ has no legal pair are left out of the forward and the merge (their partial
 would carry LSE = -inf everywhere); their backward still runs and writes zero
 gradients.  When a single shard has legal pairs -- in particular when the whole
 clean K/V is resident and passed as one range -- its forward writes the bf16
-output and the LSE directly: no fp32 partial and no merge.  This module only
+output and the LSE directly: no fp32 partial and no merge.  A whole step can
+also be captured once as a HIP graph and replayed (StepGraph), which removes
+the per-call launch cost of small, launch-bound problems.  This module only
 sequences calls and owns buffers; every arithmetic step runs in libbdattn.so.
 """
 from __future__ import annotations
