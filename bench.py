@@ -86,31 +86,84 @@ class EventTimer:
         return {k: (sum(a.elapsed_time(b) for a, b in v), len(v)) for k, v in self.events.items()}
 
 
-def cpu_baseline_bdlm(cfg, inp_cpu, n_rows: int, seed: int = 0):
-    """The fp64 oracle on a sample of query rows (KV-head group 0, every key), timed on host cores."""
+# Dense score elements (rows x keys x q-heads) the CPU baseline's sample aims at:
+# about 10-30 s of the fp64 oracle on a GPU machine's host.
+CPU_SAMPLE_ELEMS = 1.0e9
+
+
+def _f64(t):
+    import torch
+    return t.to(dtype=torch.float64).numpy()
+
+
+def cpu_baseline(cfg, inp_cpu, step_pairs: int, seed: int = 0, tasks=None):
+    """The fp64 oracle, as it stands, timed on the host cores: forward + backward of a
+    sample of the workload.  The tiny and the 4K workloads run whole (every row and
+    head); the others run the q-heads of KV group 0 on seeded-random query rows
+    against every key, sized to about CPU_SAMPLE_ELEMS dense score elements, and the
+    step time is extrapolated linearly by useful pairs.  Returns the JSON object."""
     import numpy as np
     import oracle
-    p = cfg.problem
-    G = p.h_q // p.h_kv
+    from masked_long_context_amd import workloads as wl
     rng = np.random.default_rng(seed)
-    rows = np.sort(rng.choice(p.n_q, n_rows, replace=False))
-    f64 = lambda t: t.to(dtype=__import__("torch").float64).numpy()
-    q = f64(inp_cpu["q"][:, :G])
-    do = f64(inp_cpu["dout"][:, :G])
-    kc, vc = f64(inp_cpu["k_clean"][:, :1]), f64(inp_cpu["v_clean"][:, :1])
-    kx, vx = f64(inp_cpu["k_corr"][:, :1]), f64(inp_cpu["v_corr"][:, :1])
-    prob = dict(clean_len=p.clean_len, block_size=p.block_size, q_clean_offset=p.q_clean_offset,
-                q_clean_len=p.q_clean_len, owned_blocks=list(p.owned_blocks), kv_clean_offset=0,
-                kv_clean_len=p.clean_len, with_local_corrupt=True, scale=p.scale)
+    if isinstance(cfg, wl.BdlmConfig):
+        p = cfg.problem
+        whole = p.n_q * (p.clean_len + p.n_corr) * p.h_q <= CPU_SAMPLE_ELEMS * 2
+        G = p.h_q if whole else p.h_q // p.h_kv
+        hk = p.h_kv if whole else 1
+        prob = dict(clean_len=p.clean_len, block_size=p.block_size, q_clean_offset=p.q_clean_offset,
+                    q_clean_len=p.q_clean_len, owned_blocks=list(p.owned_blocks), kv_clean_offset=0,
+                    kv_clean_len=p.clean_len, with_local_corrupt=True, scale=p.scale)
+        n_q, n_keys, hq, d = p.n_q, p.clean_len + p.n_corr, p.h_q, p.head_dim
+        q, do = _f64(inp_cpu["q"][:, :G]), _f64(inp_cpu["dout"][:, :G])
+        kc, vc = _f64(inp_cpu["k_clean"][:, :hk]), _f64(inp_cpu["v_clean"][:, :hk])
+        kx, vx = _f64(inp_cpu["k_corr"][:, :hk]), _f64(inp_cpu["v_corr"][:, :hk])
+        mask = oracle.bdlm_mask_fn(p.clean_len, p.block_size, p.q_clean_offset, p.q_clean_len, list(p.owned_blocks),
+                                   0, p.clean_len, True)
+        fwd = lambda rows: oracle.bdlm_fwd(prob, q, kc, vc, kx, vx, rows=rows)
+        bwd = lambda rows, lse, D: oracle.bdlm_bwd(prob, q, kc, vc, kx, vx, do, lse, D, rows=rows)
+    else:
+        docs = cfg.docs if tasks is not None else cfg
+        hq, d = docs.h_q, docs.head_dim
+        G, whole = hq // docs.h_kv, False
+        q, do = _f64(inp_cpu["q"][:, :G]), _f64(inp_cpu["dout"][:, :G])
+        k, v = _f64(inp_cpu["k"][:, :1]), _f64(inp_cpu["v"][:, :1])
+        n_q = q.shape[0]
+        if tasks is not None:
+            q_cu, k_cu, rows_idx = tasks
+            k, v = k[rows_idx], v[rows_idx]
+            mask = oracle.task_mask_fn(q_cu, k_cu, True)
+            fwd = lambda rows: oracle.task_fwd(q, k, v, q_cu, k_cu, True, docs.scale, rows=rows)
+            bwd = lambda rows, lse, D: oracle.task_bwd(q, k, v, do, lse, D, q_cu, k_cu, True, docs.scale, rows=rows)
+        else:
+            cu = docs.cu_seqlens
+            mask = oracle.varlen_mask_fn(cu, True)
+            fwd = lambda rows: oracle.varlen_fwd(q, k, v, cu, True, docs.scale, rows=rows)
+            bwd = lambda rows, lse, D: oracle.varlen_bwd(q, k, v, do, lse, D, cu, True, docs.scale, rows=rows)
+        n_keys = k.shape[0]
+    if whole:
+        rows = np.arange(n_q)
+    else:
+        n = int(min(n_q, max(64, CPU_SAMPLE_ELEMS // (G * n_keys))))
+        rows = np.sort(rng.choice(n_q, n, replace=False))
     t0 = time.perf_counter()
-    o, lse = oracle.bdlm_fwd(prob, q, kc, vc, kx, vx, rows=rows)
+    o, lse = fwd(rows)
     D = oracle.delta_rows(o, do[rows])
-    oracle.bdlm_bwd(prob, q, kc, vc, kx, vx, do, lse, D, rows=rows)
+    bwd(rows, lse, D)
     dt = time.perf_counter() - t0
-    m = oracle.bdlm_mask(p.clean_len, p.block_size, p.q_clean_offset, p.q_clean_len, p.owned_blocks,
-                         0, p.clean_len, True, rows=rows)
-    pairs = int(m.sum()) * G
-    return dt, pairs, len(rows)
+    pairs = sum(int(mask(rows[i:i + 4096], np.arange(n_keys)).sum()) for i in range(0, rows.size, 4096)) * G
+    rate = pairs * 14 * d / dt
+    out = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle"}
+    if whole:
+        out["sample"] = f"the whole workload ({n_q} rows x {hq} q-heads, every key), fwd+bwd in fp64; {dt:.1f} s"
+        out["extrapolated"] = False
+        out["step_s"] = round(dt, 2)
+    else:
+        out["sample"] = (f"{rows.size} seeded-random query rows x {G} q-heads (KV group 0), every key, fwd+bwd in "
+                         f"fp64: {pairs} useful pairs in {dt:.1f} s; whole-step time extrapolated by useful pairs")
+        out["extrapolated"] = True
+        out["step_s"] = round(step_pairs * hq * 14 * d / rate, 1)
+    return out
 
 
 def merge_microbench(p, n_parts: int = 16, reps: int = 5):
@@ -186,9 +239,17 @@ def bench_varlen(args, cfg):
     inp = wl.varlen_inputs(docs, seed=0)
     g = {k: v.cuda() for k, v in inp.items()}
     extra = {}
+    task_rows = None
+    t_plan = time.perf_counter()
     if tasks:
         q_cu, k_cu, src = B.cad_split(docs.cu_seqlens, cfg.max_pairs)
-        idx = torch.from_numpy(wl.task_context_rows(k_cu, src)).cuda()
+        B.Plan.tasks(q_cu, k_cu, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
+    else:
+        B.Plan.varlen(cfg.cu_seqlens, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
+    if tasks:
+        task_rows = wl.task_context_rows(k_cu, src)
+        idx = torch.from_numpy(task_rows).cuda()
         g["k"], g["v"] = g["k"].index_select(0, idx), g["v"].index_select(0, idx)
         del idx
         step = TaskStep(q_cu, k_cu, True, cfg.h_q, cfg.h_kv, cfg.head_dim)
@@ -234,7 +295,13 @@ def bench_varlen(args, cfg):
         tflops = flops / (ms * 1e-3) / 1e12
         del sg
     fwd_ms = tot["fwd"][0] / args.steps
-    bwd_ms = tot["bwd"][0] / args.steps
+    dkdv_ms = tot["dkdv"][0] / args.steps
+    dq_ms = tot["dq"][0] / args.steps
+    d = cfg.head_dim
+    dk_flops = pairs * cfg.h_q * 8 * d
+    dk_achieved = dk_flops / (dkdv_ms * 1e-3) / 1e12
+    n_keys = step.n_keys
+    dk_alg_bytes = int(2 * step.T * cfg.h_q * d * 2 + 4 * n_keys * cfg.h_kv * d * 2 + 2 * cfg.h_q * step.T * 4)
     out = {
         "metric": ("core-attention task batch (prefix contexts) fwd+bwd useful-pair TFLOP/s" if tasks else
                    "varlen packed causal attention fwd+bwd useful-pair TFLOP/s"), "value": round(tflops, 2),
@@ -244,10 +311,16 @@ def bench_varlen(args, cfg):
                    "h_kv": cfg.h_kv, "head_dim": cfg.head_dim, "useful_pairs_per_head": pairs,
                    "flops_per_step": flops, **extra},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "kernels": {"fwd": {"ms": round(fwd_ms, 4),
-                            "tflops": round(pairs * cfg.h_q * 4 * cfg.head_dim / (fwd_ms * 1e-3) / 1e12, 2)},
-                    "bwd": {"ms": round(bwd_ms, 4),
-                            "tflops_10d": round(pairs * cfg.h_q * 10 * cfg.head_dim / (bwd_ms * 1e-3) / 1e12, 2)},
+        "plan_ms": round(plan_ms, 2),
+        "roofline": {"kernel": f"dkdv_kernel<{d}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic(cfg.name), "algorithmic_bytes": dk_alg_bytes,
+                     "ms_per_launch": round(dkdv_ms, 4), "flops_per_launch": dk_flops},
+        "executed_tflops": round(pairs * cfg.h_q * 18 * d / (ms * 1e-3) / 1e12, 2),
+        "kernels": {"fwd": {"ms": round(fwd_ms, 4), "tflops": round(pairs * cfg.h_q * 4 * d / (fwd_ms * 1e-3) / 1e12, 2)},
+                    "dkdv": {"ms": round(dkdv_ms, 4), "tflops": round(dk_achieved, 2)},
+                    "dq": {"ms": round(dq_ms, 4), "tflops": round(pairs * cfg.h_q * 6 * d / (dq_ms * 1e-3) / 1e12, 2)},
+                    "cast_ms": round(tot.get("cast", (0.0, 1))[0] / args.steps, 4),
                     "prepare_ms": round(tot["prepare"][0] / args.steps, 4),
                     "finalize_ms": round(tot["finalize"][0] / args.steps, 4)},
     }
@@ -255,6 +328,10 @@ def bench_varlen(args, cfg):
         out["metric"] += " (step replayed from a HIP graph)"
         out["config"]["hip_graph"] = True
         out["graph"] = graph
+    if not args.no_cpu_baseline:
+        print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, pairs,
+                                           tasks=(q_cu, k_cu, task_rows) if tasks else None)
     print(json.dumps(out), flush=True)
 
 
@@ -292,7 +369,6 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="workloads 1-3, 5: pass the whole clean K/V as one range (all shards resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--streams", type=int, default=1,
                     help="spread the independent per-shard calls over this many streams (workloads 1-3, 5, 7)")
     ap.add_argument("--graph", action="store_true",
@@ -325,6 +401,12 @@ def main():
     # backward kernel runs once over the whole range
     shards = [(0, p.clean_len, True)] if args.fused else list(cfg.shards)
     workload = cfg.name + ("_fused_whole_range" if args.fused else "")
+    # plan building (host only, once per problem; outside the timed step)
+    from masked_long_context_amd import bdattn as B
+    t_plan = time.perf_counter()
+    for (o_, n_, loc) in shards:
+        B.Plan.from_problem(p.with_kv(o_, n_, loc))
+    plan_ms = (time.perf_counter() - t_plan) * 1e3
     step = BdlmRankStep(p, shards, streams=args.streams)
     timer = EventTimer()
     step.timer = timer
@@ -418,6 +500,7 @@ def main():
                    "clean_shards": n_sh, "useful_pairs_per_head": pairs,
                    "flops_per_step": flops},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "plan_ms": round(plan_ms, 2),
         "roofline": {"kernel": f"dkdv_kernel<{p.head_dim}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(workload), "algorithmic_bytes": dk_alg_bytes,
@@ -431,6 +514,7 @@ def main():
             "merge": {"ms": round(merge_ms / max(merge_n, 1), 4), "parts": n_act, "gbs": round(merge_gbs, 1),
                       "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4)},
             "merge_micro": merge_micro,
+            "cast_ms": round(tot.get("cast", (0.0, 1))[0] / args.steps, 4),
             "prepare_ms": round(tot.get("prepare", (0.0, 1))[0] / args.steps, 4),
             "finalize_ms": round(tot.get("finalize", (0.0, 1))[0] / args.steps, 4),
         },
@@ -449,12 +533,8 @@ def main():
     if args.config in (3, 7):
         out["exchange"] = exchange_report(p, "cp" if args.config == 7 else "csbp", len(cfg.shards))
     if not args.no_cpu_baseline:
-        print(f"# bench: cpu baseline (oracle, {args.cpu_rows} sampled rows)", file=sys.stderr, flush=True)
-        dt, spairs, nrows = cpu_baseline_bdlm(cfg, inp, args.cpu_rows)
-        out["cpu_baseline"] = {"value": round(spairs * 14 * p.head_dim / dt / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": blas_threads(), "kind": "oracle",
-                               "sample": f"{nrows} seeded-random query rows x {p.h_q // p.h_kv} q-heads "
-                                         f"(KV group 0), all keys, fwd+bwd in fp64; {dt:.1f} s"}
+        print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, pairs)
     print(json.dumps(out), flush=True)
 
 

@@ -40,6 +40,11 @@
  *   LSE, delta            [h_q][n_q] fp32
  *   packed varlen Q/O/dO  [total][h_q][head_dim], K/V [total][h_kv][head_dim]
  * Tensors are bf16 unless stated.  Device pointers must be 16-byte aligned.
+ * Sizes: query rows, keys of each segment and packed rows are each below 2^30
+ * (plans beyond that are rejected with BDATTN_EINVAL); the kernels form every
+ * element offset in 64-bit arithmetic.  The library cannot see the extent of a
+ * buffer: each must hold at least the rows the plan implies (the Python binding
+ * checks every tensor's shape, dtype, device and contiguity before each call).
  *
  * Ownership.  Every device buffer, including the workspace, belongs to the
  * caller; the library never allocates device memory.
@@ -160,6 +165,8 @@ int64_t bdattn_plan_workspace_bytes(const bdattn_plan *plan);
  * workspace size.  bdattn_plan_dkdv_split returns the value in force. */
 int bdattn_plan_set_dkdv_split(bdattn_plan *plan, int32_t split);
 int32_t bdattn_plan_dkdv_split(const bdattn_plan *plan);
+/* Head counts and head dim of the plan's problem. */
+int bdattn_plan_heads(const bdattn_plan *plan, int32_t *h_q, int32_t *h_kv, int32_t *head_dim);
 /* Legal (query, key) pairs per query head: the useful-work count. */
 int64_t bdattn_plan_useful_pairs(const bdattn_plan *plan);
 /* Query rows, and key rows of the clean (or packed) range and of the local corrupted K/V. */
@@ -179,32 +186,66 @@ int64_t bdattn_plan_n_kv(const bdattn_plan *plan, int32_t segment /* 0 clean/pac
 int64_t bdattn_plan_export(const bdattn_plan *plan, int32_t which, int32_t *out, int64_t cap);
 
 /* Forward partial of one clean K/V range (+ the local corrupted K/V when the
- * plan's problem has with_local_corrupt).  Writes O ([n_q][h_q][d], o_dtype
- * BDATTN_F32 or BDATTN_BF16) and LSE ([h_q][n_q] fp32) with `=`.
- * k_corr/v_corr may be NULL when the plan has no local corrupted keys.
- * workspace: >= bdattn_plan_workspace_bytes, 256-byte aligned. */
+ * plan's problem has with_local_corrupt).
+ * Source: "Block Parallelism For Efficient Distributed Long-Context Diffusion
+ * Language Model Training", English abstract (the clean sequence is sharded by
+ * position, so a rank meets the clean K/V one range at a time; one rank owns
+ * each corrupted block), and the rit.work explainer of CSBP, section on why
+ * conventional context parallelism sends extra data (the mask above: clean
+ * prefix of the preceding blocks plus the block's own noised version).  The
+ * partial carries its log-sum-exp so that ranges merge exactly.
+ * Computes, for every row r and q-head h over the legal keys j of this range:
+ *   LSE[h][r] = ln sum_j exp(scale q_r.k_j),  O[r][h] = sum_j exp(scale q_r.k_j - LSE) v_j
+ * (a row with no legal key in the range: O = 0, LSE = -inf).
+ * Writes O ([n_q][h_q][d], o_dtype BDATTN_F32 or BDATTN_BF16) and LSE
+ * ([h_q][n_q] fp32) with `=`.  q: [n_q][h_q][d]; k_clean/v_clean:
+ * [kv_clean_len][h_kv][d] (the range's first row); k_corr/v_corr: [n_owned*B][h_kv][d],
+ * may be NULL when the plan has no local corrupted keys.
+ * workspace: >= bdattn_plan_workspace_bytes, 256-byte aligned; each call
+ * uploads the plan's tables into it on `stream`, so calls that may overlap
+ * need separate workspaces.  Errors: EINVAL (NULL pointer, varlen plan),
+ * EALIGN (misaligned pointer), EUNSUPPORTED (o_dtype), EWORKSPACE, EHIP. */
 int bdattn_fwd(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
                const void *k_corr, const void *v_corr, void *o, int32_t o_dtype, float *lse,
                void *workspace, int64_t workspace_bytes, void *stream);
 
-/* Exact merge of n_parts partials over disjoint key sets:
+/* Exact merge of n_parts partials over disjoint key sets.
+ * Source: the block-parallelism abstract (CSBP preserves the BDLM training
+ * semantics) and the rit.work explainer's opening paragraph (the loss and the
+ * gradients do not change): the per-range partials must combine into exactly
+ * the unsharded attention, which the log-sum-exp identity gives:
  *   m = max_s LSE_s;  LSE = m + ln sum_s exp(LSE_s - m);  O = sum_s exp(LSE_s - LSE) O_s
  * (all partials -inf -> O = 0, LSE = -inf).  o_parts: [n_parts][n_rows][h][d] in
  * part_dtype, lse_parts: [n_parts][h][n_rows] fp32; o_out [n_rows][h][d] in out_dtype,
- * lse_out [h][n_rows] fp32.  d in {64, 128}. */
+ * lse_out [h][n_rows] fp32.  d in {64, 128}.  For a training step keep
+ * out_dtype BDATTN_F32 and round with bdattn_cast_f32_bf16: the backward's
+ * delta is then taken from the unrounded output.  Errors: EINVAL (n_parts < 1,
+ * NULL pointer), EALIGN, EUNSUPPORTED (d, dtype), EHIP. */
 int bdattn_lse_merge(int32_t n_parts, const void *o_parts, int32_t part_dtype, const float *lse_parts,
                      int64_t n_rows, int32_t h, int32_t d, void *o_out, int32_t out_dtype,
                      float *lse_out, void *stream);
 
 /* Backward preparation, once per rank step (shared by every K/V range):
  * delta[h][r] = sum_d dO[r][h][d] * O[r][h][d] (fp32 [h_q][n_q]) from the MERGED
- * output O (o_dtype), and, when dq_accum is not NULL, dq_accum (fp32
- * [n_q][h_q][d]) cleared to 0.  Only the plan's query side (n_q, h_q, head_dim)
- * is used. */
+ * output O (o_dtype; pass the fp32 merged output where it is kept: with one
+ * dominant key dS = P o (dP - delta) is a small difference, and the bf16
+ * rounding of O alone moves it), and, when dq_accum is not NULL, dq_accum
+ * (fp32 [n_q][h_q][d]) cleared to 0.  Only the plan's query side (n_q, h_q,
+ * head_dim) is used.  Errors: EINVAL, EALIGN, EUNSUPPORTED (o_dtype), EHIP. */
 int bdattn_bwd_prepare(const bdattn_plan *plan, const void *o, int32_t o_dtype, const void *dout,
                        float *delta, float *dq_accum, void *stream);
 
-/* Backward of one K/V range given the MERGED lse and the prepared delta:
+/* Backward of one K/V range given the MERGED lse and the prepared delta.
+ * Source: the rit.work explainer of CSBP, section on why conventional context
+ * parallelism sends extra data (CSBP returns only the gradients of the clean
+ * K/V to their owners; the corrupted K/V gradients stay with their block), and
+ * the block-parallelism abstract (training semantics preserved: with the merged
+ * LSE the probabilities of a range are exact, so per-range backwards add up to
+ * the unsharded one).
+ * Signature.  Delta is not computed here: bdattn_bwd_prepare computes it once
+ * per rank step from the merged output and every range's call reads it, so
+ * this call takes no O and no "delta ready" flag (it never writes delta).
+ * Computes:
  *   P = exp(scale Q K^T - LSE) on the legal pairs, dS = P o (dO V^T - delta)
  *   dq_accum += scale dS K    (fp32 [n_q][h_q][d]; each call adds its range)
  *   dk = scale dS^T Q, dv = P^T dO, summed over the q-heads of each KV head and
@@ -212,7 +253,8 @@ int bdattn_bwd_prepare(const bdattn_plan *plan, const void *o, int32_t o_dtype, 
  *   attends).
  * Two kernels run in order on `stream`: a key-major one for dK/dV and a
  * query-major one for dQ.  dk_corr/dv_corr may be NULL when the plan has no
- * local corrupted keys.  workspace: >= bdattn_plan_workspace_bytes. */
+ * local corrupted keys.  workspace: >= bdattn_plan_workspace_bytes.
+ * Errors: EINVAL (NULL pointer, varlen plan), EALIGN, EWORKSPACE, EHIP. */
 int bdattn_bwd(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
                const void *k_corr, const void *v_corr, const void *dout, const float *lse,
                const float *delta, float *dq_accum, void *dk_clean, void *dv_clean, void *dk_corr,
@@ -233,8 +275,12 @@ int bdattn_bwd_dq(const bdattn_plan *plan, const void *q, const void *k_clean, c
                   const float *delta, float *dq_accum, void *workspace, int64_t workspace_bytes,
                   void *stream);
 
-/* dq (bf16) = dq_accum (fp32), n_elems elements. */
+/* dq (bf16) = dq_accum (fp32), n_elems elements (round to nearest even). */
 int bdattn_dq_finalize(const float *dq_accum, void *dq, int64_t n_elems, void *stream);
+
+/* dst (bf16) = src (fp32), n_elems elements, round to nearest even: the bf16
+ * layer output from the fp32 merged output kept for the backward. */
+int bdattn_cast_f32_bf16(const float *src, void *dst, int64_t n_elems, void *stream);
 
 /* Varlen packed shards: the same kernels over a plan from bdattn_plan_create_varlen
  * or bdattn_plan_create_tasks (k and v: [n_keys][h_kv][head_dim], n_keys =

@@ -4,6 +4,13 @@ Argument marshalling only: tensors become device pointers, the stream is
 torch's current HIP stream, status codes become exceptions.  Every step of the
 computation runs in the library's HIP kernels; there is no fallback.  PyTorch
 supplies device memory and streams.
+
+The C ABI takes bare pointers, so before each call the binding checks every
+tensor against what the kernels will read and write: a device tensor on the
+stream's device, contiguous, of the documented dtype and of the exact shape
+that the plan implies (rows, keys, heads, head dim).  A mismatch raises
+BdattnError(EINVAL) (EUNSUPPORTED for a dtype) before any HIP call, so an
+undersized, strided or wrongly typed tensor never reaches a kernel.
 """
 from __future__ import annotations
 
@@ -54,6 +61,8 @@ _SIGS = {
     "bdattn_plan_dkdv_split": (c_int32, [c_void_p]),
     "bdattn_plan_n_q": (c_int64, [c_void_p]),
     "bdattn_plan_n_kv": (c_int64, [c_void_p, c_int32]),
+    "bdattn_plan_heads": (c_int32, [c_void_p, ctypes.POINTER(c_int32), ctypes.POINTER(c_int32),
+                                    ctypes.POINTER(c_int32)]),
     "bdattn_plan_export": (c_int64, [c_void_p, c_int32, c_void_p, c_int64]),
     "bdattn_fwd": (c_int32, [c_void_p] * 7 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_lse_merge": (c_int32, [c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_int32, c_void_p,
@@ -63,6 +72,7 @@ _SIGS = {
     "bdattn_bwd_dkdv": (c_int32, [c_void_p] * 14 + [c_int64, c_void_p]),
     "bdattn_bwd_dq": (c_int32, [c_void_p] * 11 + [c_int64, c_void_p]),
     "bdattn_dq_finalize": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "bdattn_cast_f32_bf16": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_fwd": (c_int32, [c_void_p] * 5 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_bwd": (c_int32, [c_void_p] * 11 + [c_int64, c_void_p]),
     "bdattn_last_error": (ctypes.c_char_p, []),
@@ -92,6 +102,60 @@ def _check(rc: int):
 
 def _ptr(t):
     return None if t is None else c_void_p(t.data_ptr())
+
+
+def _want(t, name, shape, dtypes, devs, optional=False):
+    """Check one tensor argument: dtype among `dtypes`, exactly `shape`, contiguous.
+    Its device is appended to `devs` (checked by _on_one_gpu once every tensor has
+    passed these checks)."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise BdattnError(EINVAL, f"{name} is None")
+    if not isinstance(t, torch.Tensor):
+        raise BdattnError(EINVAL, f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise BdattnError(EUNSUPPORTED, f"{name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise BdattnError(EINVAL, f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if not t.is_contiguous():
+        raise BdattnError(EINVAL, f"{name} must be contiguous")
+    devs.append((name, t.device))
+
+
+def _on_one_gpu(devs, stream):
+    """Every tensor on one GPU, and the stream (if given) on that GPU too."""
+    name0, dev0 = devs[0]
+    for name, dev in devs:
+        if dev.type != "cuda":
+            raise BdattnError(EINVAL, f"{name} must be a GPU tensor (is on {dev})")
+        if dev != dev0:
+            raise BdattnError(EINVAL, f"{name} is on {dev}, {name0} on {dev0}")
+    if stream is not None and stream.device != dev0:
+        raise BdattnError(EINVAL, f"stream is on {stream.device}, the tensors on {dev0}")
+
+
+def _bf16():
+    import torch
+    return (torch.bfloat16,)
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _bf16_or_f32():
+    import torch
+    return (torch.bfloat16, torch.float32)
+
+
+def _want_ws(ws, plan, devs):
+    import torch
+    _want(ws, "workspace", (ws.numel() if isinstance(ws, torch.Tensor) else 0,), (torch.uint8,), devs)
+    if ws.numel() < plan.workspace_bytes:
+        raise BdattnError(EWORKSPACE, f"workspace has {ws.numel()} bytes, the plan needs {plan.workspace_bytes}")
 
 
 def _stream(stream):
@@ -185,6 +249,29 @@ class Plan:
     def n_q(self) -> int:
         return lib().bdattn_plan_n_q(self._h)
 
+    @property
+    def heads(self):
+        """(h_q, h_kv, head_dim) of the plan."""
+        if getattr(self, "_heads", None) is None:
+            hq, hkv, d = c_int32(), c_int32(), c_int32()
+            _check(lib().bdattn_plan_heads(self._h, ctypes.byref(hq), ctypes.byref(hkv), ctypes.byref(d)))
+            self._heads = (hq.value, hkv.value, d.value)
+        return self._heads
+
+    def q_shape(self):
+        """Shape of Q, O, dO and dQ: (n_q, h_q, head_dim)."""
+        hq, _, d = self.heads
+        return (self.n_q, hq, d)
+
+    def kv_shape(self, segment: int):
+        """Shape of K, V, dK and dV of a key segment: (n_kv(segment), h_kv, head_dim)."""
+        _, hkv, d = self.heads
+        return (self.n_kv(segment), hkv, d)
+
+    def lse_shape(self):
+        """Shape of LSE and delta: (h_q, n_q)."""
+        return (self.heads[0], self.n_q)
+
     def n_kv(self, segment: int) -> int:
         return lib().bdattn_plan_n_kv(self._h, segment)
 
@@ -216,30 +303,103 @@ def workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _kv_args(plan, dev, k0, v0, k1, v1, g0="k_clean", g1="k_corr"):
+    """Check the K/V of both key segments; segment 1 is passed only when the plan has keys there."""
+    b = _bf16()
+    for t, nm in ((k0, g0), (v0, g0.replace("k", "v", 1))):
+        _want(t, nm, plan.kv_shape(0), b, dev)
+    if plan.n_kv(1) > 0:
+        for t, nm in ((k1, g1), (v1, g1.replace("k", "v", 1))):
+            _want(t, nm, plan.kv_shape(1), b, dev)
+        return k1, v1
+    return None, None
+
+
+def _grad_kv_args(plan, dev, dk0, dv0, dk1, dv1):
+    b = _bf16()
+    _want(dk0, "dk_clean", plan.kv_shape(0), b, dev)
+    _want(dv0, "dv_clean", plan.kv_shape(0), b, dev)
+    if plan.n_kv(1) > 0:
+        _want(dk1, "dk_corr", plan.kv_shape(1), b, dev)
+        _want(dv1, "dv_corr", plan.kv_shape(1), b, dev)
+        return dk1, dv1
+    return None, None
+
+
+def _row_args(plan, dev, lse, delta=None, dout=None):
+    _want(lse, "lse", plan.lse_shape(), _f32(), dev)
+    if delta is not None:
+        _want(delta, "delta", plan.lse_shape(), _f32(), dev)
+    if dout is not None:
+        _want(dout, "dout", plan.q_shape(), _bf16(), dev)
+
+
 def bdattn_fwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, o, lse, ws, stream=None):
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    k_corr, v_corr = _kv_args(plan, dev, k_clean, v_clean, k_corr, v_corr)
+    _want(o, "o", plan.q_shape(), _bf16_or_f32(), dev)
+    _row_args(plan, dev, lse=lse)
+    _want_ws(ws, plan, dev)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_fwd(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
                             _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def bdattn_varlen_fwd(plan: Plan, q, k, v, o, lse, ws, stream=None):
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    _kv_args(plan, dev, k, v, None, None, g0="k")
+    _want(o, "o", plan.q_shape(), _bf16_or_f32(), dev)
+    _row_args(plan, dev, lse=lse)
+    _want_ws(ws, plan, dev)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_varlen_fwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _dtype_code(o), _ptr(lse),
                                    _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def bdattn_lse_merge(o_parts, lse_parts, o_out, lse_out, stream=None):
     """o_parts [S, N, H, d], lse_parts [S, H, N] -> o_out [N, H, d], lse_out [H, N]."""
+    import torch
+    if not isinstance(o_parts, torch.Tensor) or o_parts.dim() != 4:
+        raise BdattnError(EINVAL, "o_parts must be a 4-d tensor [S, N, H, d]")
     S, N, H, D = o_parts.shape
+    dev = []
+    _want(o_parts, "o_parts", (S, N, H, D), _bf16_or_f32(), dev)
+    _want(lse_parts, "lse_parts", (S, H, N), _f32(), dev)
+    _want(o_out, "o_out", (N, H, D), _bf16_or_f32(), dev)
+    _want(lse_out, "lse_out", (H, N), _f32(), dev)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_lse_merge(S, _ptr(o_parts), _dtype_code(o_parts), _ptr(lse_parts), N, H, D,
                                   _ptr(o_out), _dtype_code(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def bdattn_bwd_prepare(plan: Plan, o, dout, delta, dq_accum=None, stream=None):
+    dev = []
+    _want(o, "o", plan.q_shape(), _bf16_or_f32(), dev)
+    _want(dout, "dout", plan.q_shape(), _bf16(), dev)
+    _want(delta, "delta", plan.lse_shape(), _f32(), dev)
+    _want(dq_accum, "dq_accum", plan.q_shape(), _f32(), dev, optional=True)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_bwd_prepare(plan.handle, _ptr(o), _dtype_code(o), _ptr(dout), _ptr(delta),
                                     _ptr(dq_accum), _stream(stream)))
 
 
+def _bwd_common(plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, ws):
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    k_corr, v_corr = _kv_args(plan, dev, k_clean, v_clean, k_corr, v_corr)
+    _row_args(plan, dev, lse=lse, delta=delta, dout=dout)
+    _want_ws(ws, plan, dev)
+    return dev, k_corr, v_corr
+
+
 def bdattn_bwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq_accum,
                dk_clean, dv_clean, dk_corr, dv_corr, ws, stream=None):
+    dev, k_corr, v_corr = _bwd_common(plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, ws)
+    _want(dq_accum, "dq_accum", plan.q_shape(), _f32(), dev)
+    dk_corr, dv_corr = _grad_kv_args(plan, dev, dk_clean, dv_clean, dk_corr, dv_corr)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_bwd(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
                             _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(dk_clean), _ptr(dv_clean),
                             _ptr(dk_corr), _ptr(dv_corr), _ptr(ws), ws.numel(), _stream(stream)))
@@ -247,23 +407,58 @@ def bdattn_bwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta
 
 def bdattn_bwd_dkdv(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta,
                     dk_clean, dv_clean, dk_corr, dv_corr, ws, stream=None):
+    dev, k_corr, v_corr = _bwd_common(plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, ws)
+    dk_corr, dv_corr = _grad_kv_args(plan, dev, dk_clean, dv_clean, dk_corr, dv_corr)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_bwd_dkdv(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
                                  _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk_clean), _ptr(dv_clean), _ptr(dk_corr),
                                  _ptr(dv_corr), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def bdattn_bwd_dq(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, dq_accum, ws, stream=None):
+    dev, k_corr, v_corr = _bwd_common(plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, delta, ws)
+    _want(dq_accum, "dq_accum", plan.q_shape(), _f32(), dev)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_bwd_dq(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
                                _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(ws), ws.numel(),
                                _stream(stream)))
 
 
 def bdattn_varlen_bwd(plan: Plan, q, k, v, dout, lse, delta, dq_accum, dk, dv, ws, stream=None):
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    _kv_args(plan, dev, k, v, None, None, g0="k")
+    _row_args(plan, dev, lse=lse, delta=delta, dout=dout)
+    _want(dq_accum, "dq_accum", plan.q_shape(), _f32(), dev)
+    _want(dk, "dk", plan.kv_shape(0), _bf16(), dev)
+    _want(dv, "dv", plan.kv_shape(0), _bf16(), dev)
+    _want_ws(ws, plan, dev)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_varlen_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
                                    _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def bdattn_cast_f32_bf16(src, dst, stream=None):
+    """dst (bf16) = src (fp32) rounded to nearest even; same shape."""
+    import torch
+    if not isinstance(src, torch.Tensor):
+        raise BdattnError(EINVAL, "src must be a torch.Tensor")
+    dev = []
+    _want(src, "src", tuple(src.shape), _f32(), dev)
+    _want(dst, "dst", tuple(src.shape), _bf16(), dev)
+    _on_one_gpu(dev, stream)
+    _check(lib().bdattn_cast_f32_bf16(_ptr(src), _ptr(dst), src.numel(), _stream(stream)))
+
+
 def bdattn_dq_finalize(dq_accum, dq, stream=None):
+    """dq (bf16) = dq_accum (fp32); same shape."""
+    import torch
+    if not isinstance(dq_accum, torch.Tensor):
+        raise BdattnError(EINVAL, "dq_accum must be a torch.Tensor")
+    dev = []
+    _want(dq_accum, "dq_accum", tuple(dq_accum.shape), _f32(), dev)
+    _want(dq, "dq", tuple(dq_accum.shape), _bf16(), dev)
+    _on_one_gpu(dev, stream)
     _check(lib().bdattn_dq_finalize(_ptr(dq_accum), _ptr(dq), dq_accum.numel(), _stream(stream)))
 
 

@@ -300,11 +300,21 @@ int bdattn_plan_set_dkdv_split(bdattn_plan *pl, int32_t split) {
     return fail(BDATTN_EINVAL, "split must be 0 (automatic) or 1.." + std::to_string(BDATTN_MAX_SPLIT));
   std::lock_guard<std::mutex> lk(pl->mu);
   if (pl->p.used) return fail(BDATTN_EINVAL, "the plan has already been used");
+  if (split > 0 && bdattn::max_grid_items(pl->p, split) > BDATTN_MAX_GRID_ITEMS)
+    return fail(BDATTN_EINVAL, "split too large: the dK/dV grid would exceed 2^32 work-items");
   bdattn::set_dkdv_split(pl->p, split);
   return BDATTN_OK;
 }
 
 int32_t bdattn_plan_dkdv_split(const bdattn_plan *pl) { return pl ? pl->p.dkdv_split : BDATTN_EINVAL; }
+
+int bdattn_plan_heads(const bdattn_plan *pl, int32_t *h_q, int32_t *h_kv, int32_t *head_dim) {
+  if (!pl || !h_q || !h_kv || !head_dim) return fail(BDATTN_EINVAL, "plan or output pointer is NULL");
+  *h_q = pl->p.h_q;
+  *h_kv = pl->p.h_kv;
+  *head_dim = pl->p.d;
+  return BDATTN_OK;
+}
 
 int64_t bdattn_plan_n_kv(const bdattn_plan *pl, int32_t seg) {
   if (!pl || seg < 0 || seg > 1) return fail(BDATTN_EINVAL, "bad plan or segment");
@@ -401,13 +411,17 @@ int bdattn_bwd_prepare(const bdattn_plan *pl, const void *o, int32_t o_dtype, co
   return BDATTN_OK;
 }
 
-int bdattn_dq_finalize(const float *acc, void *dq, int64_t n, void *stream) {
+int bdattn_cast_f32_bf16(const float *src, void *dst, int64_t n, void *stream) {
   CHECK(n >= 0, BDATTN_EINVAL, "n_elems must be >= 0");
-  CHECK_PTR(acc, n > 0);
-  CHECK_PTR(dq, n > 0);
+  CHECK_PTR(src, n > 0);
+  CHECK_PTR(dst, n > 0);
   if (n == 0) return BDATTN_OK;
-  HIP_CHECK(bdattn::launch_dq_finalize(acc, dq, n, (hipStream_t)stream), "dq finalize kernel");
+  HIP_CHECK(bdattn::launch_cast_bf16(src, dst, n, (hipStream_t)stream), "cast kernel");
   return BDATTN_OK;
+}
+
+int bdattn_dq_finalize(const float *acc, void *dq, int64_t n, void *stream) {
+  return bdattn_cast_f32_bf16(acc, dq, n, stream);
 }
 
 int bdattn_lse_merge(int32_t n_parts, const void *o_parts, int32_t part_dtype, const float *lse_parts,
@@ -418,6 +432,8 @@ int bdattn_lse_merge(int32_t n_parts, const void *o_parts, int32_t part_dtype, c
   CHECK(d == 64 || d == 128, BDATTN_EUNSUPPORTED, "d must be 64 or 128");
   CHECK(part_dtype == BDATTN_BF16 || part_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "part_dtype must be BF16 or F32");
   CHECK(out_dtype == BDATTN_BF16 || out_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "out_dtype must be BF16 or F32");
+  CHECK(n_rows * h * (d / 4) <= BDATTN_MAX_GRID_ITEMS, BDATTN_EUNSUPPORTED,
+        "n_rows * h too large for one merge launch (grid beyond 2^32 work-items)");
   const bool any = n_rows > 0;
   CHECK_PTR(o_parts, any);
   CHECK_PTR(lse_parts, any);

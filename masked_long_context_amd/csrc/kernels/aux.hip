@@ -1,7 +1,7 @@
 // Bandwidth-bound companions of the attention kernels on gfx950:
 //   prepare    delta = rowsum(dO o O) (and a clear of the dQ accumulator)
 //   merge      exact log-sum-exp merge of per-range partials
-//   finalize   fp32 dQ accumulator -> bf16
+//   cast       fp32 -> bf16 (the dQ accumulator; the merged output)
 #include "common.h"
 #include "kernels.h"
 
@@ -140,7 +140,8 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_parts, const void *op,
   if (sub == 0) lo[lidx] = lse;
 }
 
-__global__ __launch_bounds__(256) void dq_finalize_kernel(const float *acc, bf16 *out, int64_t n) {
+// Round to nearest even, 8 elements per lane.
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float *acc, bf16 *out, int64_t n) {
   const int64_t i8 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i8 + 8 <= n) {
     const f32x4 a0 = *reinterpret_cast<const f32x4 *>(acc + i8);
@@ -183,10 +184,10 @@ hipError_t launch_merge(int32_t n_parts, const void *o_parts, bool parts_f32, co
   return hipGetLastError();
 }
 
-hipError_t launch_dq_finalize(const float *acc, void *out, int64_t n, hipStream_t s) {
+hipError_t launch_cast_bf16(const float *acc, void *out, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n + 256 * 8 - 1) / (256 * 8));
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3(blocks), dim3(256), 0, s, acc, (bf16 *)out, n);
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, acc, (bf16 *)out, n);
   return hipGetLastError();
 }
 

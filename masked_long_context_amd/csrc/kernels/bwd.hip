@@ -132,12 +132,16 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   // fetch the rows' legal key bounds, wave 5 the dO tile's delta.  The tile loads
   // take 1 KB per instruction.
   float lse_reg = 0.f;
+  // The side-row buffers start at the tile's first row (64-bit pointer
+  // arithmetic), so their 32-bit record counts and offsets stay below 1 KB at
+  // any row count.
   auto side_q = [&](const TileRef &r, int b) {
-    const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
+    const int rl = lane < r.nrows ? lane : r.nrows - 1;
     if (wave == 4) {
-      lse_reg = a.lse[(int64_t)r.h * a.n_q + row];
+      lse_reg = a.lse[(int64_t)r.h * a.n_q + r.q0 + rl];
     } else if (wave == 6 || wave == 7) {
-      dword_load_lds(a.rows, a.n_q * 16, (row * 4 + 2 * s + (wave - 6)) * 4, &L.sq[b][wave - 5][0]);
+      dword_load_lds(a.rows + (int64_t)r.q0 * 4, r.nrows * 16, (rl * 4 + 2 * s + (wave - 6)) * 4,
+                     &L.sq[b][wave - 5][0]);
     }
   };
   auto lse_store = [&](int b) {   // wave 4, once its loads have landed
@@ -145,8 +149,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   };
   auto side_d = [&](const TileRef &r, int b) {
     if (wave == 5) {
-      const int row = r.q0 + (lane < r.nrows ? lane : r.nrows - 1);
-      dword_load_lds(a.delta + (int64_t)r.h * a.n_q, a.n_q * 4, row * 4, L.sd[b]);
+      const int rl = lane < r.nrows ? lane : r.nrows - 1;
+      dword_load_lds(a.delta + (int64_t)r.h * a.n_q + r.q0, r.nrows * 4, rl * 4, L.sd[b]);
     }
   };
   auto tile_q = [&](const TileRef &r, int b) {
@@ -400,6 +404,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
 // waves, one per SIMD with the whole register file).
 constexpr int kDkdvKT = 1;
 constexpr int kDkdvThreads = 2 * (4 / kDkdvKT) * 64;
+static_assert(kDkdvThreads == BDATTN_DKDV_THREADS, "dK/dV workgroup size known to the scheduler");
 
 template <int D>
 __global__ __launch_bounds__(kDkdvThreads, 1) void dkdv_kernel(BwdArgs a) {

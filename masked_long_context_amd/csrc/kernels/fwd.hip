@@ -27,7 +27,8 @@ namespace bdattn {
 namespace {
 
 // 64-row LDS tiles of K (and of V) per key step of the forward.
-constexpr int kFwdTiles = 2;
+constexpr int kFwdTiles = BDATTN_FWD_STEP / 64;
+static_assert(kFwdTiles * 64 == BDATTN_FWD_STEP, "forward step = whole LDS tiles");
 
 template <int D>
 __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void fwd_kernel(FwdArgs a) {

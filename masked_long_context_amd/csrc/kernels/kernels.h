@@ -53,6 +53,6 @@ hipError_t launch_prepare(const PrepArgs &a, int32_t d, hipStream_t s);
 hipError_t launch_merge(int32_t n_parts, const void *o_parts, bool parts_f32, const float *lse_parts,
                         int64_t n_rows, int32_t h, int32_t d, void *o_out, bool out_f32, float *lse_out,
                         hipStream_t s);
-hipError_t launch_dq_finalize(const float *acc, void *out, int64_t n, hipStream_t s);
+hipError_t launch_cast_bf16(const float *src, void *out, int64_t n, hipStream_t s);
 
 }  // namespace bdattn

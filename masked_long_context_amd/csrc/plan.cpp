@@ -65,7 +65,8 @@ void tile_regions(Plan &p, const std::vector<Region> &regions) {
     for (int64_t q0 = g.begin; q0 < g.end; q0 += BDATTN_FWD_BM) {
       TileDesc t{};
       summarize(p.rows, q0, std::min<int64_t>(BDATTN_FWD_BM, g.end - q0), t);
-      t.cost = tiles_in(t.seg[0], BDATTN_FWD_BN) + tiles_in(t.seg[1], BDATTN_FWD_BN);
+      // cost = key steps of the forward's walk
+      t.cost = tiles_in(t.seg[0], BDATTN_FWD_STEP) + tiles_in(t.seg[1], BDATTN_FWD_STEP);
       p.fwd.push_back(t);
     }
     for (int64_t q0 = g.begin; q0 < g.end; q0 += BDATTN_BWD_BM) {
@@ -125,7 +126,7 @@ void build_bwd_lists(Plan &p) {
   });
 }
 
-void finish(Plan &p) {
+std::string finish(Plan &p) {
   p.useful_pairs = 0;
   for (int64_t r = 0; r < p.n_q; ++r)
     for (int s = 0; s < 2; ++s)
@@ -161,7 +162,10 @@ void finish(Plan &p) {
   if (!p.lrec.empty()) std::memcpy(p.image.data() + h.off_lrec, p.lrec.data(), p.lrec.size() * 4);
 
   set_dkdv_split(p, 0);
+  if (max_grid_items(p, p.dkdv_split) > BDATTN_MAX_GRID_ITEMS)
+    return "UNSUP:problem too large: a kernel's grid would exceed 2^32 work-items (split the rows or heads)";
   p.id = g_next_id.fetch_add(1);
+  return "";
 }
 
 std::string check_heads(int32_t h_q, int32_t h_kv, int32_t d) {
@@ -172,6 +176,17 @@ std::string check_heads(int32_t h_q, int32_t h_kv, int32_t d) {
 }
 
 }  // namespace
+
+// Largest grid (work-items) of any kernel that runs on this plan, with `split`
+// dK/dV workgroups per key tile: forward and dQ (one workgroup per query tile
+// and q-head), dK/dV (per key tile, KV head and share), backward preparation
+// (D/8 threads per row and q-head).
+int64_t max_grid_items(const Plan &p, int32_t split) {
+  const int64_t fwd = (int64_t)p.fwd.size() * p.h_q * 64 * BDATTN_FWD_WAVES;
+  const int64_t dkdv = (int64_t)p.kt.size() * p.h_kv * split * BDATTN_DKDV_THREADS;
+  const int64_t prep = p.n_q * p.h_q * (p.d / 8);
+  return std::max(fwd, std::max(dkdv, prep));
+}
 
 // Splitting a key tile's walk over several workgroups only pays when the
 // kernel would otherwise leave compute units idle: small problems have few key
@@ -188,7 +203,8 @@ void set_dkdv_split(Plan &p, int32_t split) {
     if (n_wg > 0 && n_wg < BDATTN_SPLIT_TARGET / 2) {
       f = std::min<int64_t>(BDATTN_MAX_SPLIT, (BDATTN_SPLIT_TARGET + n_wg - 1) / n_wg);
       f = std::min<int64_t>(f, longest / BDATTN_SPLIT_MIN_ITERS);
-      while (f > 1 && f * part > BDATTN_SPLIT_MAX_BYTES) --f;
+      while (f > 1 && (f * part > BDATTN_SPLIT_MAX_BYTES || max_grid_items(p, (int32_t)f) > BDATTN_MAX_GRID_ITEMS))
+        --f;
     }
     split = (int32_t)std::max<int64_t>(1, f);
   }
@@ -251,8 +267,7 @@ std::string build_bdlm(Plan &p, int64_t L, int32_t B, int64_t q_off, int64_t q_l
     }
   }
   tile_regions(p, {Region{0, q_len}, Region{q_len, n_q}});
-  finish(p);
-  return "";
+  return finish(p);
 }
 
 std::string build_tasks(Plan &p, const int32_t *q_cu, const int32_t *k_cu, int32_t n, bool causal, int32_t h_q,
@@ -286,8 +301,7 @@ std::string build_tasks(Plan &p, const int32_t *q_cu, const int32_t *k_cu, int32
     if (q_len > 0) regions.push_back(Region{q_cu[t], q_cu[t + 1]});
   }
   tile_regions(p, regions);
-  finish(p);
-  return "";
+  return finish(p);
 }
 
 int64_t cad_split(const int32_t *cu, int32_t n_docs, int64_t max_pairs, int32_t *q_cu, int32_t *k_cu,
@@ -346,8 +360,7 @@ std::string build_varlen(Plan &p, const int32_t *cu, int32_t n_seqs, bool causal
     if (cu[s + 1] > cu[s]) regions.push_back(Region{cu[s], cu[s + 1]});
   }
   tile_regions(p, regions);
-  finish(p);
-  return "";
+  return finish(p);
 }
 
 }  // namespace bdattn

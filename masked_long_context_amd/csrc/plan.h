@@ -72,5 +72,7 @@ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // Sets the dK/dV split factor (0: automatic, else 1 .. BDATTN_MAX_SPLIT) and the
 // workspace layout that follows from it.
 void set_dkdv_split(Plan &p, int32_t split);
+// Largest number of work-items any kernel's grid would hold on this plan.
+int64_t max_grid_items(const Plan &p, int32_t split);
 
 }  // namespace bdattn

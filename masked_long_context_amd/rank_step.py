@@ -7,12 +7,17 @@ Training", English abstract).  The step runs, on the caller's HIP stream (or,
 optionally, with its independent per-shard calls spread over several streams):
 
     for each clean K/V shard s:  bdattn_fwd  -> partial (O_s, LSE_s)
-    bdattn_lse_merge             -> O, LSE
-    bdattn_bwd_prepare           -> delta, cleared dQ accumulator
+    bdattn_lse_merge             -> O (fp32), LSE
+    bdattn_cast_f32_bf16         -> O (bf16, the layer output)
+    bdattn_bwd_prepare           -> delta = rowsum(dO o O) from the fp32 O, cleared dQ accumulator
     for each clean K/V shard s:  bdattn_bwd_dkdv -> dK_s, dV_s; bdattn_bwd_dq -> dQ (accumulated)
     bdattn_dq_finalize           -> dQ (bf16)
 
-The local corrupted K/V join the call of one chosen shard.  Shards whose plan
+The merged output is kept in fp32 until the backward: delta is a row sum of
+dO o O, and dS = P o (dP - delta) is a small difference wherever one key
+dominates a row, so rounding O to bf16 before that sum would cost dK accuracy
+on peaked softmax rows (exact_delta=False takes delta from the bf16 O instead
+and keeps no fp32 copy).  The local corrupted K/V join the call of one chosen shard.  Shards whose plan
 has no legal pair are left out of the forward and the merge (their partial
 would carry LSE = -inf everywhere); their backward still runs and writes zero
 gradients.  When a single shard has legal pairs -- in particular when the whole
@@ -33,7 +38,7 @@ from . import bdattn as B
 
 class BdlmRankStep:
     def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda",
-                 part_dtype=torch.float32, dkdv_split: int = 0, streams: int = 1):
+                 part_dtype=torch.float32, dkdv_split: int = 0, streams: int = 1, exact_delta: bool = True):
         self.problem = problem
         self.shards = list(shards)
         self.device = device
@@ -58,6 +63,9 @@ class BdlmRankStep:
         self.o_parts = torch.empty((n_parts, self.n_q, self.h_q, self.d), dtype=part_dtype, device=device)
         self.lse_parts = torch.empty((n_parts, self.h_q, self.n_q), dtype=torch.float32, device=device)
         self.o = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.bfloat16, device=device)
+        # fp32 merged output kept for the backward's delta (None: delta from the bf16 O)
+        self.o32 = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.float32, device=device) \
+            if exact_delta else None
         self.lse = torch.empty((self.h_q, self.n_q), dtype=torch.float32, device=device)
         self.delta = torch.empty((self.h_q, self.n_q), dtype=torch.float32, device=device)
         self.dq_acc = torch.empty((self.n_q, self.h_q, self.d), dtype=torch.float32, device=device)
@@ -96,17 +104,25 @@ class BdlmRankStep:
         for s in self.side:
             main.wait_stream(s)
 
+    def _to_bf16(self):
+        if self.o32 is not None:
+            with self._t("cast"):
+                B.bdattn_cast_f32_bf16(self.o32, self.o)
+
     def forward(self, q, k_clean, v_clean, k_corr, v_corr):
+        out = self.o32 if self.o32 is not None else self.o
         if not self.active:
-            self.o.zero_()
+            out.zero_()
             self.lse.fill_(float("-inf"))
+            self._to_bf16()
             return self.o, self.lse
         if self.direct:
             i = self.active[0]
             off, n, local = self.shards[i]
             with self._t("fwd"):
                 B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
-                             k_corr if local else None, v_corr if local else None, self.o, self.lse, self.ws)
+                             k_corr if local else None, v_corr if local else None, out, self.lse, self.ws)
+            self._to_bf16()
             return self.o, self.lse
         self._fork()
         for slot, i in enumerate(self.active):
@@ -118,13 +134,14 @@ class BdlmRankStep:
                              self.o_parts[slot], self.lse_parts[slot], ws)
         self._join()
         with self._t("merge"):
-            B.bdattn_lse_merge(self.o_parts[:len(self.active)], self.lse_parts[:len(self.active)],
-                               self.o, self.lse)
+            B.bdattn_lse_merge(self.o_parts[:len(self.active)], self.lse_parts[:len(self.active)], out, self.lse)
+        self._to_bf16()
         return self.o, self.lse
 
     def backward(self, q, k_clean, v_clean, k_corr, v_corr, dout):
         with self._t("prepare"):
-            B.bdattn_bwd_prepare(self.plans[0], self.o, dout, self.delta, self.dq_acc)
+            B.bdattn_bwd_prepare(self.plans[0], self.o32 if self.o32 is not None else self.o, dout, self.delta,
+                                 self.dq_acc)
         # the two steps of bdattn_bwd, called apart so that each can be timed
         self._fork()
         for i, (off, n, local) in enumerate(self.shards):
@@ -178,13 +195,16 @@ class StepGraph:
 class VarlenStep:
     """Forward + backward of packed independent shards (one call each)."""
 
-    def __init__(self, cu_seqlens, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0, plan=None):
+    def __init__(self, cu_seqlens, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0, plan=None,
+                 exact_delta: bool = True):
         self.plan = plan if plan is not None else B.Plan.varlen(cu_seqlens, causal, h_q, h_kv, head_dim,
                                                                 softmax_scale)
         T, n_keys = self.plan.n_q, self.plan.n_kv(0)
         self.T, self.n_keys, self.h_q, self.h_kv, self.d = T, n_keys, h_q, h_kv, head_dim
         self.ws = B.workspace(self.plan.workspace_bytes, device)
         self.o = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
+        # fp32 output kept for the backward's delta (see BdlmRankStep)
+        self.o32 = torch.empty((T, h_q, head_dim), dtype=torch.float32, device=device) if exact_delta else None
         self.lse = torch.empty((h_q, T), dtype=torch.float32, device=device)
         self.delta = torch.empty((h_q, T), dtype=torch.float32, device=device)
         self.dq_acc = torch.empty((T, h_q, head_dim), dtype=torch.float32, device=device)
@@ -203,15 +223,23 @@ class VarlenStep:
 
     def forward(self, q, k, v):
         with self._t("fwd"):
-            B.bdattn_varlen_fwd(self.plan, q, k, v, self.o, self.lse, self.ws)
+            B.bdattn_varlen_fwd(self.plan, q, k, v, self.o32 if self.o32 is not None else self.o, self.lse,
+                                self.ws)
+        if self.o32 is not None:
+            with self._t("cast"):
+                B.bdattn_cast_f32_bf16(self.o32, self.o)
         return self.o, self.lse
 
     def backward(self, q, k, v, dout):
         with self._t("prepare"):
-            B.bdattn_bwd_prepare(self.plan, self.o, dout, self.delta, self.dq_acc)
-        with self._t("bwd"):
-            B.bdattn_varlen_bwd(self.plan, q, k, v, dout, self.lse, self.delta, self.dq_acc,
-                                self.dk, self.dv, self.ws)
+            B.bdattn_bwd_prepare(self.plan, self.o32 if self.o32 is not None else self.o, dout, self.delta,
+                                 self.dq_acc)
+        # the two kernels of bdattn_varlen_bwd, called apart so that each can be timed
+        with self._t("dkdv"):
+            B.bdattn_bwd_dkdv(self.plan, q, k, v, None, None, dout, self.lse, self.delta, self.dk, self.dv,
+                              None, None, self.ws)
+        with self._t("dq"):
+            B.bdattn_bwd_dq(self.plan, q, k, v, None, None, dout, self.lse, self.delta, self.dq_acc, self.ws)
         with self._t("finalize"):
             B.bdattn_dq_finalize(self.dq_acc, self.dq)
         return self.dq, self.dk, self.dv
@@ -226,6 +254,8 @@ class TaskStep(VarlenStep):
     key context (packed task queries [q_cu[-1], h_q, d], packed contexts
     [k_cu[-1], h_kv, d]); dk/dv hold one gradient per context row."""
 
-    def __init__(self, q_cu, k_cu, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0):
+    def __init__(self, q_cu, k_cu, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0,
+                 exact_delta: bool = True):
         plan = B.Plan.tasks(q_cu, k_cu, causal, h_q, h_kv, head_dim, softmax_scale)
-        super().__init__(None, causal, h_q, h_kv, head_dim, device, softmax_scale, plan=plan)
+        super().__init__(None, causal, h_q, h_kv, head_dim, device, softmax_scale, plan=plan,
+                         exact_delta=exact_delta)

@@ -86,11 +86,12 @@ def poison_(*ts):
             t.fill_(float("nan"))
 
 
-def run_gpu_bdlm(cfg: wl.BdlmConfig, inp, shards=None, poison=True, dkdv_split=0) -> dict:
+def run_gpu_bdlm(cfg: wl.BdlmConfig, inp, shards=None, poison=True, dkdv_split=0, exact_delta=True) -> dict:
     g = {k: v.to("cuda") for k, v in inp.items()}
-    step = BdlmRankStep(cfg.problem, shards if shards is not None else cfg.shards, dkdv_split=dkdv_split)
+    step = BdlmRankStep(cfg.problem, shards if shards is not None else cfg.shards, dkdv_split=dkdv_split,
+                        exact_delta=exact_delta)
     if poison:
-        poison_(step.o_parts, step.lse_parts, step.o, step.lse, step.delta, step.dq_acc, step.dq,
+        poison_(step.o_parts, step.lse_parts, step.o, step.o32, step.lse, step.delta, step.dq_acc, step.dq,
                 step.dk_clean, step.dv_clean, step.dk_corr, step.dv_corr)
     step.step(g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
     torch.cuda.synchronize()
@@ -109,7 +110,7 @@ def run_gpu_varlen(cu, causal, h_q, h_kv, d, inp, poison=True) -> dict:
     g = {k: v.to("cuda") for k, v in inp.items()}
     step = VarlenStep(cu, causal, h_q, h_kv, d)
     if poison:
-        poison_(step.o, step.lse, step.delta, step.dq_acc, step.dq, step.dk, step.dv)
+        poison_(step.o, step.o32, step.lse, step.delta, step.dq_acc, step.dq, step.dk, step.dv)
     step.step(g["q"], g["k"], g["v"], g["dout"])
     torch.cuda.synchronize()
     return dict(o=step.o, lse=step.lse, dq=step.dq, dk=step.dk, dv=step.dv, step=step)
@@ -127,7 +128,7 @@ def run_gpu_tasks(q_cu, k_cu, causal, h_q, h_kv, d, inp, poison=True) -> dict:
     g = {k: v.to("cuda") for k, v in inp.items()}
     step = TaskStep(q_cu, k_cu, causal, h_q, h_kv, d)
     if poison:
-        poison_(step.o, step.lse, step.delta, step.dq_acc, step.dq, step.dk, step.dv)
+        poison_(step.o, step.o32, step.lse, step.delta, step.dq_acc, step.dq, step.dk, step.dv)
     step.step(g["q"], g["k"], g["v"], g["dout"])
     torch.cuda.synchronize()
     return dict(o=step.o, lse=step.lse, dq=step.dq, dk=step.dk, dv=step.dv, step=step)

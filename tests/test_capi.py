@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["bdattn_fwd", "bdattn_bwd", "bdattn_lse_merge", "bdattn_varlen_fwd", "bdattn_varlen_bwd",
               "bdattn_plan_create", "bdattn_plan_create_varlen", "bdattn_bwd_prepare", "bdattn_dq_finalize",
-              "bdattn_plan_create_tasks", "bdattn_cad_split"]:
+              "bdattn_plan_create_tasks", "bdattn_cad_split", "bdattn_cast_f32_bf16", "bdattn_plan_heads"]:
         assert n in names
 
 
@@ -109,73 +109,152 @@ def test_cad_split_rejects():
     assert lib.bdattn_cad_split(cu, 2, 10, None, None, None, 0) == 3
 
 
-class FakeTensor:
-    """Stands in for a device tensor: only data_ptr/numel/dtype are read before validation fails."""
-
-    def __init__(self, addr, numel=1 << 40, dtype=None):
-        import torch
-        self._a, self._n = addr, numel
-        self.dtype = dtype or torch.bfloat16
-
-    def data_ptr(self):
-        return self._a
-
-    def numel(self):
-        return self._n
-
-
-class FakeStream:
-    cuda_stream = 0
+def _addr(a):
+    return ctypes.c_void_p(a)
 
 
 def test_fwd_argument_errors_before_any_hip_call():
-    import torch
+    """C-level validation of bdattn_fwd / bdattn_varlen_fwd (fake device addresses: every
+    call below fails before the library touches them)."""
+    lib = B.lib()
     plan = B.Plan.bdlm(**_problem())
-    good = FakeTensor(1 << 20)
-    f32 = FakeTensor(1 << 20, dtype=torch.float32)
-    ws_small = FakeTensor(1 << 20, numel=16)
-    call = lambda **kw: B.bdattn_fwd(plan, **{**dict(q=good, k_clean=good, v_clean=good, k_corr=good,
-                                                   v_corr=good, o=f32, lse=f32, ws=good,
-                                                   stream=FakeStream()), **kw})
-    assert _status(lambda: call(q=None)) == B.EINVAL
-    assert _status(lambda: call(k_corr=None)) == B.EINVAL          # plan has local corrupted keys
-    assert _status(lambda: call(q=FakeTensor((1 << 20) + 8))) == B.EALIGN
-    assert _status(lambda: call(ws=FakeTensor((1 << 20) + 16))) == B.EALIGN
-    assert _status(lambda: call(ws=ws_small)) == B.EWORKSPACE
-    assert _status(lambda: call(o=FakeTensor(1 << 20, dtype=torch.float16))) == B.EUNSUPPORTED
+    good = 1 << 20
+    ws_n = plan.workspace_bytes
+    args = dict(q=good, k_clean=good, v_clean=good, k_corr=good, v_corr=good, o=good, o_dtype=B.F32, lse=good,
+                ws=good, ws_bytes=ws_n)
+
+    def call(**kw):
+        a = {**args, **kw}
+        ptr = lambda x: None if x is None else _addr(x)
+        return lib.bdattn_fwd(plan.handle, ptr(a["q"]), ptr(a["k_clean"]), ptr(a["v_clean"]), ptr(a["k_corr"]),
+                              ptr(a["v_corr"]), ptr(a["o"]), a["o_dtype"], ptr(a["lse"]), ptr(a["ws"]),
+                              a["ws_bytes"], None)
+
+    assert call(q=None) == B.EINVAL
+    assert call(k_corr=None) == B.EINVAL          # the plan has local corrupted keys
+    assert call(q=good + 8) == B.EALIGN
+    assert call(ws=good + 16) == B.EALIGN
+    assert call(ws_bytes=16) == B.EWORKSPACE
+    assert call(o_dtype=7) == B.EUNSUPPORTED
     # a varlen plan is refused by the BDLM entry point and vice versa
     vplan = B.Plan.varlen([0, 100], True, 4, 2, 128)
-    assert _status(lambda: B.bdattn_fwd(vplan, good, good, good, good, good, f32, f32, good,
-                                        stream=FakeStream())) == B.EINVAL
-    assert _status(lambda: B.bdattn_varlen_fwd(plan, good, good, good, f32, f32, good,
-                                               stream=FakeStream())) == B.EINVAL
+    p_ = _addr(good)
+    assert lib.bdattn_fwd(vplan.handle, p_, p_, p_, p_, p_, p_, B.F32, p_, p_, vplan.workspace_bytes, None) == B.EINVAL
+    assert lib.bdattn_varlen_fwd(plan.handle, p_, p_, p_, p_, B.F32, p_, p_, ws_n, None) == B.EINVAL
 
 
 def test_bwd_and_prepare_argument_errors():
+    lib = B.lib()
+    plan = B.Plan.bdlm(**_problem())
+    good = 1 << 20
+    names = ["q", "k_clean", "v_clean", "k_corr", "v_corr", "dout", "lse", "delta", "dq_accum", "dk_clean",
+             "dv_clean", "dk_corr", "dv_corr", "ws"]
+    base = {n: good for n in names}
+
+    def call(fn, skip=(), ws_bytes=None, **kw):
+        a = {**base, **kw}
+        ptrs = [None if a[n] is None else _addr(a[n]) for n in names if n not in skip]
+        return fn(plan.handle, *ptrs, plan.workspace_bytes if ws_bytes is None else ws_bytes, None)
+
+    assert call(lib.bdattn_bwd, dk_clean=None) == B.EINVAL
+    assert call(lib.bdattn_bwd, dv_corr=None) == B.EINVAL
+    assert call(lib.bdattn_bwd, ws_bytes=8) == B.EWORKSPACE
+    assert call(lib.bdattn_bwd, lse=good + 4) == B.EALIGN
+    dk_skip = ("dq_accum",)
+    assert call(lib.bdattn_bwd_dkdv, skip=dk_skip, dk_corr=None) == B.EINVAL
+    assert call(lib.bdattn_bwd_dkdv, skip=dk_skip, ws_bytes=8) == B.EWORKSPACE
+    dq_skip = ("dk_clean", "dv_clean", "dk_corr", "dv_corr")
+    assert call(lib.bdattn_bwd_dq, skip=dq_skip, dq_accum=None) == B.EINVAL
+    assert call(lib.bdattn_bwd_dq, skip=dq_skip, delta=good + 4) == B.EALIGN
+    vplan = B.Plan.varlen([0, 100], True, 4, 2, 128)
+    p_ = _addr(good)
+    assert lib.bdattn_bwd(vplan.handle, *([p_] * 14), vplan.workspace_bytes, None) == B.EINVAL
+    # preparation: NULL output / input, unsupported O dtype
+    assert lib.bdattn_bwd_prepare(plan.handle, None, B.BF16, p_, p_, p_, None) == B.EINVAL
+    assert lib.bdattn_bwd_prepare(plan.handle, p_, B.BF16, p_, None, None, None) == B.EINVAL
+    assert lib.bdattn_bwd_prepare(plan.handle, p_, 5, p_, p_, None, None) == B.EUNSUPPORTED
+    assert lib.bdattn_bwd_prepare(None, p_, B.BF16, p_, p_, None, None) == B.EINVAL
+
+
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_checks_every_tensor_before_the_call():
+    """The ctypes binding checks dtype, shape (from the plan), contiguity and device
+    of every tensor before calling into the library (CPU tensors: the device check
+    is the last one, so each earlier rejection is reachable here)."""
     import torch
     plan = B.Plan.bdlm(**_problem())
-    good = FakeTensor(1 << 20)
-    f32 = FakeTensor(1 << 20, dtype=torch.float32)
-    st = FakeStream()
-    args = dict(q=good, k_clean=good, v_clean=good, k_corr=good, v_corr=good, dout=good, lse=f32,
-                delta=f32, dq_accum=f32, dk_clean=good, dv_clean=good, dk_corr=good,
-                dv_corr=good, ws=good, stream=st)
-    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "dk_clean": None})) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "dv_corr": None})) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "ws": FakeTensor(1 << 20, numel=8)})) == B.EWORKSPACE
-    assert _status(lambda: B.bdattn_bwd(plan, **{**args, "lse": FakeTensor((1 << 20) + 4)})) == B.EALIGN
-    assert _status(lambda: B.bdattn_bwd_prepare(plan, None, good, f32, f32, st)) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd_prepare(plan, good, good, None, None, st)) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd_prepare(plan, FakeTensor(1 << 20, dtype=torch.float16), good, f32,
-                                                None, st)) == B.EUNSUPPORTED
-    vplan = B.Plan.varlen([0, 100], True, 4, 2, 128)
-    assert _status(lambda: B.bdattn_bwd(vplan, **args)) == B.EINVAL
-    dk_args = {k: v for k, v in args.items() if k != "dq_accum"}
-    assert _status(lambda: B.bdattn_bwd_dkdv(plan, **{**dk_args, "dk_corr": None})) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd_dkdv(plan, **{**dk_args, "ws": FakeTensor(1 << 20, numel=8)})) == B.EWORKSPACE
-    dq_args = {k: v for k, v in args.items() if k not in ("dk_clean", "dv_clean", "dk_corr", "dv_corr")}
-    assert _status(lambda: B.bdattn_bwd_dq(plan, **{**dq_args, "dq_accum": None})) == B.EINVAL
-    assert _status(lambda: B.bdattn_bwd_dq(plan, **{**dq_args, "delta": FakeTensor((1 << 20) + 4)})) == B.EALIGN
+    n_q, hq, d = plan.q_shape()
+    assert (n_q, hq, d) == (128, 4, 128) and plan.heads == (4, 2, 128)
+    kv0, kv1 = plan.kv_shape(0), plan.kv_shape(1)
+    assert kv0 == (128, 2, 128) and kv1 == (64, 2, 128)
+    f32 = torch.float32
+    ok = dict(q=_cpu((n_q, hq, d)), k_clean=_cpu(kv0), v_clean=_cpu(kv0), k_corr=_cpu(kv1), v_corr=_cpu(kv1),
+              o=_cpu((n_q, hq, d), f32), lse=_cpu((hq, n_q), f32), ws=_cpu((plan.workspace_bytes,), torch.uint8))
+    fwd = lambda **kw: B.bdattn_fwd(plan, **{**ok, **kw})
+
+    def err(fn, code, text):
+        with pytest.raises(B.BdattnError) as e:
+            fn()
+        assert e.value.status == code, (e.value, code)
+        assert text in str(e.value), (str(e.value), text)
+
+    err(lambda: fwd(q=_cpu((n_q, hq, d), f32)), B.EUNSUPPORTED, "q has dtype")
+    err(lambda: fwd(q=_cpu((n_q - 1, hq, d))), B.EINVAL, "q has shape")
+    err(lambda: fwd(k_clean=_cpu((kv0[0] - 32,) + kv0[1:])), B.EINVAL, "k_clean has shape")
+    err(lambda: fwd(v_corr=_cpu((kv1[0] + 32,) + kv1[1:])), B.EINVAL, "v_corr has shape")
+    err(lambda: fwd(k_corr=None), B.EINVAL, "k_corr is None")
+    err(lambda: fwd(o=_cpu((n_q, hq, d), torch.float16)), B.EUNSUPPORTED, "o has dtype")
+    err(lambda: fwd(lse=_cpu((n_q, hq), f32)), B.EINVAL, "lse has shape")
+    err(lambda: fwd(q=_cpu((n_q, d, hq)).transpose(1, 2)), B.EINVAL, "q must be contiguous")
+    err(lambda: fwd(ws=_cpu((plan.workspace_bytes,), f32)), B.EUNSUPPORTED, "workspace has dtype")
+    err(lambda: fwd(q="not a tensor"), B.EINVAL, "must be a torch.Tensor")
+    err(lambda: fwd(), B.EINVAL, "must be a GPU tensor")
+    # backward: the row side (dout, lse, delta, dq_accum) and the gradients follow the plan too
+    bw = dict(q=ok["q"], k_clean=ok["k_clean"], v_clean=ok["v_clean"], k_corr=ok["k_corr"], v_corr=ok["v_corr"],
+              dout=_cpu((n_q, hq, d)), lse=ok["lse"], delta=_cpu((hq, n_q), f32), dq_accum=_cpu((n_q, hq, d), f32),
+              dk_clean=_cpu(kv0), dv_clean=_cpu(kv0), dk_corr=_cpu(kv1), dv_corr=_cpu(kv1), ws=ok["ws"])
+    bwd = lambda **kw: B.bdattn_bwd(plan, **{**bw, **kw})
+    err(lambda: bwd(dout=_cpu((n_q, hq, d), f32)), B.EUNSUPPORTED, "dout has dtype")
+    err(lambda: bwd(delta=_cpu((hq, n_q + 1), f32)), B.EINVAL, "delta has shape")
+    err(lambda: bwd(dq_accum=_cpu((n_q, hq, d))), B.EUNSUPPORTED, "dq_accum has dtype")
+    err(lambda: bwd(dk_clean=_cpu((kv0[0], 1, d))), B.EINVAL, "dk_clean has shape")
+    err(lambda: bwd(dv_corr=None), B.EINVAL, "dv_corr is None")
+    err(lambda: bwd(), B.EINVAL, "must be a GPU tensor")
+    err(lambda: B.bdattn_bwd_prepare(plan, ok["o"], bw["dout"], _cpu((hq, n_q))), B.EUNSUPPORTED, "delta has dtype")
+    # merge: partial shapes follow o_parts
+    S = 3
+    op, lp = _cpu((S, n_q, hq, d), f32), _cpu((S, hq, n_q), f32)
+    err(lambda: B.bdattn_lse_merge(op, _cpu((S, n_q, hq), f32), ok["o"], ok["lse"]), B.EINVAL, "lse_parts has shape")
+    err(lambda: B.bdattn_lse_merge(op, lp, _cpu((n_q, hq, d - 1), f32), ok["lse"]), B.EINVAL, "o_out has shape")
+    err(lambda: B.bdattn_lse_merge(op[:, :, :, :64], lp, ok["o"], ok["lse"]), B.EINVAL, "contiguous")
+    err(lambda: B.bdattn_dq_finalize(ok["o"], _cpu((n_q, hq, d + 8))), B.EINVAL, "dq has shape")
+    err(lambda: B.bdattn_cast_f32_bf16(ok["o"], _cpu((n_q, hq, d), f32)), B.EUNSUPPORTED, "dst has dtype")
+    # varlen: K/V and gradients follow the packed key count
+    vplan = B.Plan.varlen([0, 100, 164], True, 4, 2, 128)
+    vq, vk = _cpu(vplan.q_shape()), _cpu(vplan.kv_shape(0))
+    err(lambda: B.bdattn_varlen_fwd(vplan, vq, _cpu((100, 2, 128)), vk, _cpu(vplan.q_shape(), f32),
+                                    _cpu(vplan.lse_shape(), f32), _cpu((vplan.workspace_bytes,), torch.uint8)),
+        B.EINVAL, "k has shape")
+
+
+def test_plans_beyond_the_size_limits_are_rejected():
+    """Row and key counts of 2^30 or more, and grids beyond 2^32 work-items, never
+    reach a kernel (the rejection happens before any table is built)."""
+    lim = 1 << 30
+    assert _status(lambda: B.Plan.varlen([0, lim], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.tasks([0, lim], [0, 1], True, 4, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.Plan.bdlm(**_problem(clean_len=2 * lim, block_size=1 << 20, q_clean_offset=0,
+                                                  q_clean_len=lim, owned_blocks=[], kv_clean_len=1 << 20))) == B.EINVAL
+    assert _status(lambda: B.Plan.bdlm(**_problem(clean_len=2 * lim, block_size=1 << 20, q_clean_offset=0,
+                                                  q_clean_len=1 << 20, owned_blocks=[], kv_clean_len=lim))) == B.EINVAL
+    # 2^22 rows in 256-row shards x 4096 q-heads: the forward grid would hold
+    # 2^22 / 256 * 4096 * 512 = 2^35 work-items
+    cu = np.arange(0, (1 << 22) + 1, 256, dtype=np.int32)
+    assert _status(lambda: B.Plan.varlen(cu, True, 4096, 1, 64)) == B.EUNSUPPORTED
 
 
 def test_merge_and_finalize_argument_errors():
@@ -189,6 +268,10 @@ def test_merge_and_finalize_argument_errors():
                                 None) == B.EALIGN
     assert lib.bdattn_dq_finalize(None, p, 100, None) == B.EINVAL
     assert lib.bdattn_dq_finalize(p, p, -1, None) == B.EINVAL
+    assert lib.bdattn_cast_f32_bf16(p, None, 100, None) == B.EINVAL
+    assert lib.bdattn_cast_f32_bf16(ctypes.c_void_p((1 << 20) + 2), p, 100, None) == B.EALIGN
+    # n_rows * h * d / 4 threads beyond 2^32 work-items
+    assert lib.bdattn_lse_merge(2, p, B.F32, p, 1 << 28, 2, 128, p, B.BF16, p, None) == B.EUNSUPPORTED
     # nothing to do is not an error and touches no device
     assert lib.bdattn_lse_merge(2, None, B.F32, None, 0, 2, 128, None, B.BF16, None, None) == B.OK
     assert lib.bdattn_dq_finalize(None, None, 0, None) == B.OK
