@@ -209,6 +209,23 @@ int bdattn_fwd(const bdattn_plan *plan, const void *q, const void *k_clean, cons
                const void *k_corr, const void *v_corr, void *o, int32_t o_dtype, float *lse,
                void *workspace, int64_t workspace_bytes, void *stream);
 
+/* bdattn_fwd for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * results as bdattn_fwd (BDLM plans), without the workspace: the plan's
+ * forward tables are copied into a static device array of 8 MiB that the
+ * library holds on each GPU it runs on until the process ends, so the call
+ * allocates nothing (no hipMalloc, no pinned copy; the tables are copied from
+ * the plan's host memory on `stream`).  Limit: the forward tables (16 bytes per
+ * query row plus 48 per 256-row tile, about 500K query rows) must fit in
+ * 8 MiB, else BDATTN_EWORKSPACE before any HIP call.  Every call on a GPU
+ * shares that GPU's array, which keeps the last call's tables: calls that may
+ * overlap on one GPU (other streams, other threads) race on it and must be
+ * ordered by the caller.  The device is the current one; the stream must
+ * belong to it. */
+int bdattn_fwd_static(const bdattn_plan *plan, const void *q, const void *k_clean, const void *v_clean,
+                      const void *k_corr, const void *v_corr, void *o, int32_t o_dtype, float *lse,
+                      void *stream);
+
 /* Exact merge of n_parts partials over disjoint key sets.
  * Source: the block-parallelism abstract (CSBP preserves the BDLM training
  * semantics) and the rit.work explainer's opening paragraph (the loss and the

@@ -65,6 +65,7 @@ _SIGS = {
                                     ctypes.POINTER(c_int32)]),
     "bdattn_plan_export": (c_int64, [c_void_p, c_int32, c_void_p, c_int64]),
     "bdattn_fwd": (c_int32, [c_void_p] * 7 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
+    "bdattn_fwd_static": (c_int32, [c_void_p] * 7 + [c_int32, c_void_p, c_void_p]),
     "bdattn_lse_merge": (c_int32, [c_int32, c_void_p, c_int32, c_void_p, c_int64, c_int32, c_int32, c_void_p,
                                    c_int32, c_void_p, c_void_p]),
     "bdattn_bwd_prepare": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -344,6 +345,20 @@ def bdattn_fwd(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, o, lse, ws, stre
     _on_one_gpu(dev, stream)
     _check(lib().bdattn_fwd(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
                             _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def bdattn_fwd_static(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, o, lse, stream=None):
+    """bdattn_fwd without a workspace: the plan's forward tables go into the library's
+    static per-GPU scratch array (no allocation anywhere in the call).  Calls that may
+    overlap on one GPU race on that array."""
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    k_corr, v_corr = _kv_args(plan, dev, k_clean, v_clean, k_corr, v_corr)
+    _want(o, "o", plan.q_shape(), _bf16_or_f32(), dev)
+    _row_args(plan, dev, lse=lse)
+    _on_one_gpu(dev, stream)
+    _check(lib().bdattn_fwd_static(plan.handle, _ptr(q), _ptr(k_clean), _ptr(v_clean), _ptr(k_corr), _ptr(v_corr),
+                                   _ptr(o), _dtype_code(o), _ptr(lse), _stream(stream)))
 
 
 def bdattn_varlen_fwd(plan: Plan, q, k, v, o, lse, ws, stream=None):

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libbdattn.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["plan.cpp", "capi.cpp", "kernels/fwd.hip", "kernels/bwd.hip", "kernels/aux.hip"]
+SOURCES = ["plan.cpp", "capi.cpp", "noalloc.hip", "kernels/fwd.hip", "kernels/bwd.hip", "kernels/aux.hip"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",

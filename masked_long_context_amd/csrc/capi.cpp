@@ -13,19 +13,28 @@
 #include "kernels/kernels.h"
 #include "plan.h"
 
-struct bdattn_plan {
-  bdattn::Plan p;
-  std::mutex mu;   // guards the lazily made pinned copy of the tables
-};
+#include "capi_internal.h"
 
 namespace {
 
 thread_local std::string g_err;
 
+}  // namespace
+
+namespace bdattn {
+namespace abi {
+
 int fail(int code, const std::string &msg) {
   g_err = msg;
   return code;
 }
+
+}  // namespace abi
+}  // namespace bdattn
+
+namespace {
+
+using bdattn::abi::fail;
 
 int fail_build(const std::string &e) {
   if (e.rfind("ALIGN:", 0) == 0) return fail(BDATTN_EALIGN, e.substr(6));
@@ -92,9 +101,14 @@ const int32_t *img(const void *base, int64_t off) {
   return reinterpret_cast<const int32_t *>((const char *)base + off);
 }
 
-int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
-            const void *v1, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
-  bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
+}  // namespace
+
+namespace bdattn {
+namespace abi {
+
+int check_fwd_args(const bdattn_plan *pl, const void *q, const void *k0, const void *v0, const void *k1,
+                   const void *v1, const void *o, int32_t o_dtype, const float *lse) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
   const bdattn::Plan &p = pl->p;
   CHECK(o_dtype == BDATTN_BF16 || o_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "o_dtype must be BF16 or F32");
   const bool rows = p.n_q > 0;
@@ -105,12 +119,13 @@ int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   CHECK_PTR(v0, p.n_seg[0] > 0);
   CHECK_PTR(k1, p.n_seg[1] > 0);
   CHECK_PTR(v1, p.n_seg[1] > 0);
-  int rc = check_ws(p, ws, ws_bytes);
-  if (rc != BDATTN_OK) return rc;
-  if (!rows) return BDATTN_OK;
-  hipStream_t s = (hipStream_t)stream;
-  rc = upload(pl, ws, s);
-  if (rc != BDATTN_OK) return rc;
+  return BDATTN_OK;
+}
+
+int launch_fwd_on_tables(const bdattn_plan *pl, const void *tables, const void *q, const void *k0, const void *v0,
+                         const void *k1, const void *v1, void *o, int32_t o_dtype, float *lse, hipStream_t s) {
+  const bdattn::Plan &p = pl->p;
+  const void *ws = tables;
   bdattn::FwdArgs a{};
   a.k[0] = k0;
   a.k[1] = k1;
@@ -132,6 +147,27 @@ int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   a.scale_log2 = p.scale * 1.4426950408889634f;
   HIP_CHECK(bdattn::launch_fwd(a, p.d, s), "forward kernel");
   return BDATTN_OK;
+}
+
+int64_t fwd_table_bytes(const bdattn_plan *pl) { return pl->p.hdr.off_bq; }
+
+}  // namespace abi
+}  // namespace bdattn
+
+namespace {
+
+int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
+            const void *v1, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
+  bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
+  int rc = bdattn::abi::check_fwd_args(pl, q, k0, v0, k1, v1, o, o_dtype, lse);
+  if (rc != BDATTN_OK) return rc;
+  rc = check_ws(pl->p, ws, ws_bytes);
+  if (rc != BDATTN_OK) return rc;
+  if (pl->p.n_q == 0) return BDATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  rc = upload(pl, ws, s);
+  if (rc != BDATTN_OK) return rc;
+  return bdattn::abi::launch_fwd_on_tables(pl, ws, q, k0, v0, k1, v1, o, o_dtype, lse, s);
 }
 
 int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
