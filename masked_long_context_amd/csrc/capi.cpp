@@ -2,7 +2,7 @@
 // codes, thread-local error text, table uploads and kernel launches.
 #include "bdattn.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstring>

@@ -1,6 +1,6 @@
 // Internals shared by the C ABI's source files (not part of the public header).
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <mutex>
 #include <string>

@@ -1,6 +1,6 @@
 // Kernel argument blocks and launchers (internal to the library).
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace bdattn {

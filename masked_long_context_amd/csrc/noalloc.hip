@@ -4,6 +4,8 @@
 // the plan's forward tables, which bdattn_fwd uploads into the caller's
 // workspace, go into a file-scope device array instead, so the call takes no
 // workspace and allocates nothing.
+#include <hip/hip_runtime.h>
+
 #include "capi_internal.h"
 
 namespace {
