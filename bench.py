@@ -223,6 +223,37 @@ def gemm_ceiling(n: int = 8192, seconds: float = 1.0):
             "ms": round(ms, 1), "tflops": round(2.0 * n ** 3 * reps / (ms * 1e-3) / 1e12, 1)}
 
 
+def atomics_rate(n_q: int, h_q: int, d: int, src_rows: int = 1 << 22, reps: int = 5):
+    """fp32 atomic-add rate of this GPU on the pattern a fused key-major backward
+    would use for dQ: blocks of 64 (row, head) rows of d fp32 values, each added
+    into a random 64-row block of an [n_q * h_q, d] accumulator (torch's
+    index_add_, which adds with one fp32 atomic per element).  Returns the rate
+    and what one atomic per useful pair and q-head (d / 128 per pair at 128 keys
+    per workgroup) would cost."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    n_dst = n_q * h_q
+    dst = torch.zeros((n_dst, d), device="cuda", dtype=torch.float32)
+    src = torch.randn((src_rows, d), generator=gen, device="cuda", dtype=torch.float32)
+    blocks = torch.randint(0, n_dst // 64, (src_rows // 64,), generator=gen, device="cuda")
+    index = (blocks[:, None] * 64 + torch.arange(64, device="cuda")[None, :]).reshape(-1)
+    dst.index_add_(0, index, src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.index_add_(0, index, src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    n_atomics = src_rows * d
+    del dst, src, index, blocks
+    torch.cuda.empty_cache()
+    return {"kind": "fp32 atomic add (torch index_add_), 64-row blocks into random 64-row blocks of a "
+                    f"[{n_dst}, {d}] accumulator", "atomics": n_atomics, "ms": round(ms, 4),
+            "g_atomics_per_s": round(n_atomics / (ms * 1e-3) / 1e9, 1)}
+
+
 def bench_varlen(args, cfg):
     """The varlen workload (packed token-causal shards) or its core-attention task
     form (the same documents cut into tasks that carry their prefix context,
@@ -376,6 +407,9 @@ def main():
                          "workloads); value is then the replay rate, the eager figures stay beside it")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the sustained-MFMA ceiling measurement (vendor bf16 GEMM, about 1 s)")
+    ap.add_argument("--atomics", action="store_true",
+                    help="also measure the fp32 atomic-add rate on a dQ-shaped accumulator (what a fused backward "
+                         "with atomic dQ would pay instead of the dQ kernel's recompute)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -530,6 +564,15 @@ def main():
         ceiling["kernel_fracs"] = {k: round(v["tflops"] / ceiling["tflops"], 4) for k, v in per.items()}
         ceiling["step_executed_frac"] = round(out["executed_tflops"] / ceiling["tflops"], 4)
         out["roofline"]["sustained_ceiling"] = ceiling
+    if args.atomics:
+        at = atomics_rate(p.n_q, p.h_q, p.head_dim)
+        # a fused key-major backward adds dQ with d / 128 atomics per useful pair and
+        # q-head (one 64 x d block per 64 x 128 tile of pairs)
+        need = pairs * p.h_q * p.head_dim / 128
+        at["fused_dq_atomics_per_step"] = int(need)
+        at["fused_dq_atomics_ms_per_step"] = round(need / (at["g_atomics_per_s"] * 1e9) * 1e3, 1)
+        at["dq_kernel_ms_per_step"] = round(per["dq"]["ms_per_step"], 2)
+        out["atomics"] = at
     if args.config in (3, 7):
         out["exchange"] = exchange_report(p, "cp" if args.config == 7 else "csbp", len(cfg.shards))
     if not args.no_cpu_baseline:
