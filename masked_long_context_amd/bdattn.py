@@ -232,7 +232,7 @@ class Plan:
 
     @property
     def workspace_bytes(self) -> int:
-        return lib().bdattn_plan_workspace_bytes(self._h)
+        return lib().bdattn_plan_workspace_bytes(self._h)   # changes with set_dkdv_split
 
     @property
     def useful_pairs(self) -> int:
@@ -248,7 +248,9 @@ class Plan:
 
     @property
     def n_q(self) -> int:
-        return lib().bdattn_plan_n_q(self._h)
+        if getattr(self, "_n_q", None) is None:
+            self._n_q = lib().bdattn_plan_n_q(self._h)
+        return self._n_q
 
     @property
     def heads(self):
@@ -274,7 +276,11 @@ class Plan:
         return (self.heads[0], self.n_q)
 
     def n_kv(self, segment: int) -> int:
-        return lib().bdattn_plan_n_kv(self._h, segment)
+        """Key rows of segment 0 (clean range / packed keys) or 1 (local corrupted K/V).
+        A plan is immutable, so its sizes are read from the library once."""
+        if getattr(self, "_n_kv", None) is None:
+            self._n_kv = (lib().bdattn_plan_n_kv(self._h, 0), lib().bdattn_plan_n_kv(self._h, 1))
+        return self._n_kv[segment]
 
     def export(self, which: int) -> np.ndarray:
         width = {0: 4, 1: 12, 2: 12, 3: 4, 4: 1}[which]
@@ -475,6 +481,70 @@ def bdattn_dq_finalize(dq_accum, dq, stream=None):
     _want(dq, "dq", tuple(dq_accum.shape), _bf16(), dev)
     _on_one_gpu(dev, stream)
     _check(lib().bdattn_dq_finalize(_ptr(dq_accum), _ptr(dq), dq_accum.numel(), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- unchecked calls
+# The entry points above without the per-tensor checks, for a caller that owns
+# its output buffers and checks its inputs against its plans once per step (the
+# steps of rank_step.py): a Python check costs microseconds of host time per
+# tensor, as long as a small kernel runs, and a small step is then bound by the
+# host.  The library's own argument validation still runs on every call.
+# Tensors are passed as torch tensors (or None); `stream` as a raw HIP stream.
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def current_stream_handle():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def fwd_unchecked(plan, q, kc, vc, kx, vx, o, lse, ws, stream):
+    _check(lib().bdattn_fwd(plan.handle, _p(q), _p(kc), _p(vc), _p(kx), _p(vx), _p(o), _dtype_code(o), _p(lse),
+                            _p(ws), ws.numel(), stream))
+
+
+def varlen_fwd_unchecked(plan, q, k, v, o, lse, ws, stream):
+    _check(lib().bdattn_varlen_fwd(plan.handle, _p(q), _p(k), _p(v), _p(o), _dtype_code(o), _p(lse), _p(ws),
+                                   ws.numel(), stream))
+
+
+def lse_merge_unchecked(o_parts, lse_parts, o_out, lse_out, stream):
+    S, N, H, D = o_parts.shape
+    _check(lib().bdattn_lse_merge(S, _p(o_parts), _dtype_code(o_parts), _p(lse_parts), N, H, D, _p(o_out),
+                                  _dtype_code(o_out), _p(lse_out), stream))
+
+
+def bwd_prepare_unchecked(plan, o, dout, delta, dq_accum, stream):
+    _check(lib().bdattn_bwd_prepare(plan.handle, _p(o), _dtype_code(o), _p(dout), _p(delta), _p(dq_accum), stream))
+
+
+def bwd_dkdv_unchecked(plan, q, kc, vc, kx, vx, dout, lse, delta, dkc, dvc, dkx, dvx, ws, stream):
+    _check(lib().bdattn_bwd_dkdv(plan.handle, _p(q), _p(kc), _p(vc), _p(kx), _p(vx), _p(dout), _p(lse), _p(delta),
+                                 _p(dkc), _p(dvc), _p(dkx), _p(dvx), _p(ws), ws.numel(), stream))
+
+
+def bwd_dq_unchecked(plan, q, kc, vc, kx, vx, dout, lse, delta, dq_accum, ws, stream):
+    _check(lib().bdattn_bwd_dq(plan.handle, _p(q), _p(kc), _p(vc), _p(kx), _p(vx), _p(dout), _p(lse), _p(delta),
+                               _p(dq_accum), _p(ws), ws.numel(), stream))
+
+
+def cast_unchecked(src, dst, stream):
+    _check(lib().bdattn_cast_f32_bf16(_p(src), _p(dst), src.numel(), stream))
+
+
+def dq_finalize_unchecked(dq_accum, dq, stream):
+    _check(lib().bdattn_dq_finalize(_p(dq_accum), _p(dq), dq_accum.numel(), stream))
+
+
+def check_inputs(named, devs=None):
+    """Check (tensor, name, shape, dtypes) tuples as the public calls do, and that
+    all of them sit on one GPU: used once per step by callers of the unchecked calls."""
+    devs = [] if devs is None else devs
+    for t, name, shape, dtypes in named:
+        _want(t, name, shape, dtypes, devs)
+    _on_one_gpu(devs, None)
 
 
 def cad_split(cu_seqlens, max_pairs_per_task: int):

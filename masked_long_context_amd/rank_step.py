@@ -75,6 +75,7 @@ class BdlmRankStep:
         self.dk_corr = torch.empty((p.n_corr, self.h_kv, self.d), dtype=torch.bfloat16, device=device)
         self.dv_corr = torch.empty_like(self.dk_corr)
         self.timer = None      # optional callable(tag) -> context manager around each library call
+        self._main = None      # raw handle of the caller's stream during a forward or backward
 
     @property
     def useful_pairs(self) -> int:
@@ -91,8 +92,8 @@ class BdlmRankStep:
         import contextlib
         k = j % (len(self.side) + 1)
         if k == 0:
-            return contextlib.nullcontext(), self.ws
-        return torch.cuda.stream(self.side[k - 1]), self.ws_side[k - 1]
+            return contextlib.nullcontext(), self.ws, self._main
+        return torch.cuda.stream(self.side[k - 1]), self.ws_side[k - 1], self.side[k - 1].cuda_stream
 
     def _fork(self):
         main = torch.cuda.current_stream()
@@ -107,9 +108,28 @@ class BdlmRankStep:
     def _to_bf16(self):
         if self.o32 is not None:
             with self._t("cast"):
-                B.bdattn_cast_f32_bf16(self.o32, self.o)
+                B.cast_unchecked(self.o32, self.o, self._main)
+
+    def check_inputs(self, q, k_clean, v_clean, k_corr, v_corr, dout=None):
+        """The caller's tensors against the problem (once per call of forward or
+        backward; the library calls of the step then go unchecked)."""
+        p = self.problem
+        bf = (torch.bfloat16,)
+        kv = (p.clean_len, self.h_kv, self.d)
+        named = [(q, "q", (self.n_q, self.h_q, self.d), bf), (k_clean, "k_clean", kv, bf), (v_clean, "v_clean", kv, bf)]
+        if p.n_corr:
+            cr = (p.n_corr, self.h_kv, self.d)
+            named += [(k_corr, "k_corr", cr, bf), (v_corr, "v_corr", cr, bf)]
+        if dout is not None:
+            named.append((dout, "dout", (self.n_q, self.h_q, self.d), bf))
+        B.check_inputs(named, [("o", self.o.device)])
 
     def forward(self, q, k_clean, v_clean, k_corr, v_corr):
+        self.check_inputs(q, k_clean, v_clean, k_corr, v_corr)
+        return self._forward(q, k_clean, v_clean, k_corr, v_corr)
+
+    def _forward(self, q, k_clean, v_clean, k_corr, v_corr):
+        self._main = B.current_stream_handle()
         out = self.o32 if self.o32 is not None else self.o
         if not self.active:
             out.zero_()
@@ -120,49 +140,57 @@ class BdlmRankStep:
             i = self.active[0]
             off, n, local = self.shards[i]
             with self._t("fwd"):
-                B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
-                             k_corr if local else None, v_corr if local else None, out, self.lse, self.ws)
+                B.fwd_unchecked(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
+                                k_corr if local else None, v_corr if local else None, out, self.lse, self.ws,
+                                self._main)
             self._to_bf16()
             return self.o, self.lse
         self._fork()
         for slot, i in enumerate(self.active):
             off, n, local = self.shards[i]
-            lane, ws = self._lane(slot)
+            lane, ws, st = self._lane(slot)
             with lane, self._t("fwd"):
-                B.bdattn_fwd(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
-                             k_corr if local else None, v_corr if local else None,
-                             self.o_parts[slot], self.lse_parts[slot], ws)
+                B.fwd_unchecked(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
+                                k_corr if local else None, v_corr if local else None,
+                                self.o_parts[slot], self.lse_parts[slot], ws, st)
         self._join()
         with self._t("merge"):
-            B.bdattn_lse_merge(self.o_parts[:len(self.active)], self.lse_parts[:len(self.active)], out, self.lse)
+            B.lse_merge_unchecked(self.o_parts[:len(self.active)], self.lse_parts[:len(self.active)], out, self.lse,
+                                  self._main)
         self._to_bf16()
         return self.o, self.lse
 
     def backward(self, q, k_clean, v_clean, k_corr, v_corr, dout):
+        self.check_inputs(q, k_clean, v_clean, k_corr, v_corr, dout)
+        return self._backward(q, k_clean, v_clean, k_corr, v_corr, dout)
+
+    def _backward(self, q, k_clean, v_clean, k_corr, v_corr, dout):
+        self._main = B.current_stream_handle()
         with self._t("prepare"):
-            B.bdattn_bwd_prepare(self.plans[0], self.o32 if self.o32 is not None else self.o, dout, self.delta,
-                                 self.dq_acc)
+            B.bwd_prepare_unchecked(self.plans[0], self.o32 if self.o32 is not None else self.o, dout, self.delta,
+                                    self.dq_acc, self._main)
         # the two steps of bdattn_bwd, called apart so that each can be timed
         self._fork()
         for i, (off, n, local) in enumerate(self.shards):
             kc, vc = k_clean[off:off + n], v_clean[off:off + n]
             kx, vx = (k_corr, v_corr) if local else (None, None)
-            lane, ws = self._lane(i)
+            lane, ws, st = self._lane(i)
             with lane, self._t("dkdv"):
-                B.bdattn_bwd_dkdv(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta,
-                                  self.dk_clean[off:off + n], self.dv_clean[off:off + n],
-                                  self.dk_corr if local else None, self.dv_corr if local else None, ws)
+                B.bwd_dkdv_unchecked(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta,
+                                     self.dk_clean[off:off + n], self.dv_clean[off:off + n],
+                                     self.dk_corr if local else None, self.dv_corr if local else None, ws, st)
             with self._t("dq"):
-                B.bdattn_bwd_dq(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta, self.dq_acc,
-                                self.ws)
+                B.bwd_dq_unchecked(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta, self.dq_acc,
+                                   self.ws, self._main)
         self._join()
         with self._t("finalize"):
-            B.bdattn_dq_finalize(self.dq_acc, self.dq)
+            B.dq_finalize_unchecked(self.dq_acc, self.dq, self._main)
         return self.dq, self.dk_clean, self.dv_clean, self.dk_corr, self.dv_corr
 
     def step(self, q, k_clean, v_clean, k_corr, v_corr, dout):
-        self.forward(q, k_clean, v_clean, k_corr, v_corr)
-        return self.backward(q, k_clean, v_clean, k_corr, v_corr, dout)
+        self.check_inputs(q, k_clean, v_clean, k_corr, v_corr, dout)
+        self._forward(q, k_clean, v_clean, k_corr, v_corr)
+        return self._backward(q, k_clean, v_clean, k_corr, v_corr, dout)
 
 
 class StepGraph:
@@ -221,32 +249,51 @@ class VarlenStep:
         import contextlib
         return self.timer(tag) if self.timer is not None else contextlib.nullcontext()
 
+    def check_inputs(self, q, k, v, dout=None):
+        bf = (torch.bfloat16,)
+        kv = (self.n_keys, self.h_kv, self.d)
+        named = [(q, "q", (self.T, self.h_q, self.d), bf), (k, "k", kv, bf), (v, "v", kv, bf)]
+        if dout is not None:
+            named.append((dout, "dout", (self.T, self.h_q, self.d), bf))
+        B.check_inputs(named, [("o", self.o.device)])
+
     def forward(self, q, k, v):
+        self.check_inputs(q, k, v)
+        return self._forward(q, k, v)
+
+    def _forward(self, q, k, v):
+        st = B.current_stream_handle()
         with self._t("fwd"):
-            B.bdattn_varlen_fwd(self.plan, q, k, v, self.o32 if self.o32 is not None else self.o, self.lse,
-                                self.ws)
+            B.varlen_fwd_unchecked(self.plan, q, k, v, self.o32 if self.o32 is not None else self.o, self.lse,
+                                   self.ws, st)
         if self.o32 is not None:
             with self._t("cast"):
-                B.bdattn_cast_f32_bf16(self.o32, self.o)
+                B.cast_unchecked(self.o32, self.o, st)
         return self.o, self.lse
 
     def backward(self, q, k, v, dout):
+        self.check_inputs(q, k, v, dout)
+        return self._backward(q, k, v, dout)
+
+    def _backward(self, q, k, v, dout):
+        st = B.current_stream_handle()
         with self._t("prepare"):
-            B.bdattn_bwd_prepare(self.plan, self.o32 if self.o32 is not None else self.o, dout, self.delta,
-                                 self.dq_acc)
+            B.bwd_prepare_unchecked(self.plan, self.o32 if self.o32 is not None else self.o, dout, self.delta,
+                                    self.dq_acc, st)
         # the two kernels of bdattn_varlen_bwd, called apart so that each can be timed
         with self._t("dkdv"):
-            B.bdattn_bwd_dkdv(self.plan, q, k, v, None, None, dout, self.lse, self.delta, self.dk, self.dv,
-                              None, None, self.ws)
+            B.bwd_dkdv_unchecked(self.plan, q, k, v, None, None, dout, self.lse, self.delta, self.dk, self.dv,
+                                 None, None, self.ws, st)
         with self._t("dq"):
-            B.bdattn_bwd_dq(self.plan, q, k, v, None, None, dout, self.lse, self.delta, self.dq_acc, self.ws)
+            B.bwd_dq_unchecked(self.plan, q, k, v, None, None, dout, self.lse, self.delta, self.dq_acc, self.ws, st)
         with self._t("finalize"):
-            B.bdattn_dq_finalize(self.dq_acc, self.dq)
+            B.dq_finalize_unchecked(self.dq_acc, self.dq, st)
         return self.dq, self.dk, self.dv
 
     def step(self, q, k, v, dout):
-        self.forward(q, k, v)
-        return self.backward(q, k, v, dout)
+        self.check_inputs(q, k, v, dout)
+        self._forward(q, k, v)
+        return self._backward(q, k, v, dout)
 
 
 class TaskStep(VarlenStep):
