@@ -11,6 +11,8 @@ and 10d in the backward (QK^T recompute, dO V^T, P^T dO, dS^T Q, dS K).
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 
 Prints one JSON line.  --gpus N with N > 1 is refused: this path runs on one GPU.
+With the CPU baseline (the default), the line also carries "parity": the errors of
+the step's outputs against the oracle's on the baseline's sample.
 
 The roofline entry's "traffic" (HBM bytes per launch of the dK/dV kernel) comes
 from rocprofv3 FETCH_SIZE and WRITE_SIZE passes recorded in profiles/; it is
@@ -149,8 +151,9 @@ def cpu_baseline(cfg, inp_cpu, step_pairs: int, seed: int = 0, tasks=None):
     t0 = time.perf_counter()
     o, lse = fwd(rows)
     D = oracle.delta_rows(o, do[rows])
-    bwd(rows, lse, D)
+    dq, dk, dv = bwd(rows, lse, D)
     dt = time.perf_counter() - t0
+    ref = dict(rows=rows, G=G, o=o, lse=lse, dq=dq, dk=dk if whole else None, dv=dv if whole else None)
     pairs = sum(int(mask(rows[i:i + 4096], np.arange(n_keys)).sum()) for i in range(0, rows.size, 4096)) * G
     rate = pairs * 14 * d / dt
     out = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle"}
@@ -163,7 +166,39 @@ def cpu_baseline(cfg, inp_cpu, step_pairs: int, seed: int = 0, tasks=None):
                          f"fp64: {pairs} useful pairs in {dt:.1f} s; whole-step time extrapolated by useful pairs")
         out["extrapolated"] = True
         out["step_s"] = round(step_pairs * hq * 14 * d / rate, 1)
-    return out
+    return out, ref
+
+
+def parity_report(ref, o, lse, dq, dk=None, dv=None):
+    """Errors of the GPU step's outputs against the oracle's on the CPU baseline's
+    sample (its rows, q-heads of KV group 0; every output when the workload ran whole):
+    max-abs and relative L2 of O, dQ (and dK, dV), max-abs of LSE over finite rows."""
+    import numpy as np
+    import torch
+    rows, G = ref["rows"], ref["G"]
+    idx = torch.from_numpy(rows)
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+
+    def err(got, want):
+        diff = got - want
+        n = float(np.linalg.norm(want))
+        return {"max_abs": float(f"{np.abs(diff).max():.3e}"),
+                "rel_l2": float(f"{(np.linalg.norm(diff) / n if n else np.linalg.norm(diff)):.3e}")}
+
+    rep = {"rows": int(rows.size), "q_heads": int(G), "o": err(f64(o.index_select(0, idx.to(o.device))[:, :G]), ref["o"]),
+           "dq": err(f64(dq.index_select(0, idx.to(dq.device))[:, :G]), ref["dq"])}
+    gl = f64(lse[:G].index_select(1, idx.to(lse.device)))
+    fin = np.isfinite(ref["lse"])
+    rep["lse_max_abs"] = float(f"{np.abs(gl[fin] - ref['lse'][fin]).max():.3e}") if fin.any() else 0.0
+    rep["lse_neginf_match"] = bool(np.array_equal(np.isneginf(gl), np.isneginf(ref["lse"])))
+    if ref["dk"] is not None and dk is not None:
+        hk = ref["dk"].shape[1]
+        rep["dk"] = err(f64(dk[:, :hk]), ref["dk"])
+        rep["dv"] = err(f64(dv[:, :hk]), ref["dv"])
+    tol = lambda e: e["max_abs"] <= 2e-2 and e["rel_l2"] <= 5e-3
+    rep["within_tolerance"] = bool(all(tol(rep[k]) for k in ("o", "dq", "dk", "dv") if k in rep)
+                                   and rep["lse_max_abs"] <= 1e-5 and rep["lse_neginf_match"])
+    return rep
 
 
 def merge_microbench(p, n_parts: int = 16, reps: int = 5):
@@ -361,8 +396,8 @@ def bench_varlen(args, cfg):
         out["graph"] = graph
     if not args.no_cpu_baseline:
         print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, pairs,
-                                           tasks=(q_cu, k_cu, task_rows) if tasks else None)
+        out["cpu_baseline"], ref = cpu_baseline(cfg, inp, pairs, tasks=(q_cu, k_cu, task_rows) if tasks else None)
+        out["parity"] = parity_report(ref, step.o, step.lse, step.dq)
     print(json.dumps(out), flush=True)
 
 
@@ -577,7 +612,9 @@ def main():
         out["exchange"] = exchange_report(p, "cp" if args.config == 7 else "csbp", len(cfg.shards))
     if not args.no_cpu_baseline:
         print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, pairs)
+        out["cpu_baseline"], ref = cpu_baseline(cfg, inp, pairs)
+        out["parity"] = parity_report(ref, step.o, step.lse, step.dq, torch.cat([step.dk_clean, step.dk_corr]),
+                                      torch.cat([step.dv_clean, step.dv_corr]))
     print(json.dumps(out), flush=True)
 
 
