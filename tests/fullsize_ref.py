@@ -99,6 +99,40 @@ def rows_reference(q, k, v, dout, mask_fn: MaskFn, scale: float, rows: Sequence[
     return rows, o, lse, dq
 
 
+def group_reference(q, k, v, dout, mask_fn: MaskFn, scale: float, piece: int = PIECE,
+                    threads: Optional[int] = None):
+    """Every output of one KV-head group: O [N, H_q, d], LSE [H_q, N], dQ [N, H_q, d]
+    and dK, dV [M, H_kv, d] over all N rows and M keys, in one pass over row chunks.
+    Each (row chunk, key piece) pair with a legal key gives its dQ contribution and
+    the piece's dK/dV contribution (``oracle.attention_bwd`` with the chunk's merged
+    LSE and delta); the latter is added into the piece's rows under a per-piece lock."""
+    import threading
+    n, m = q.shape[0], k.shape[0]
+    pieces = _pieces(m, piece)
+    locks = [threading.Lock() for _ in pieces]
+    dk = np.zeros((m, k.shape[1], k.shape[2]))
+    dv = np.zeros_like(dk)
+    starts = list(range(0, n, ROW_CHUNK))
+
+    def work(r0):
+        rr = np.arange(r0, min(n, r0 + ROW_CHUNK), dtype=np.int64)
+        o, lse, used = _chunk_fwd(q, k, v, mask_fn, scale, rr, pieces)
+        D = oracle.delta_rows(o, dout[rr])
+        dq = np.zeros_like(o)
+        for (a, b) in used:
+            d_piece, dk_p, dv_p = oracle.attention_bwd(q, k[a:b], v[a:b], dout, lse, D, shifted_mask(mask_fn, a),
+                                                       scale, rows=rr)
+            dq += d_piece
+            with locks[pieces.index((a, b))]:
+                dk[a:b] += dk_p
+                dv[a:b] += dv_p
+        return o, lse, dq
+
+    res = _pool_map(work, starts, threads)
+    return (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res], axis=1),
+            np.concatenate([r[2] for r in res]), dk, dv)
+
+
 def lse_delta_all_rows(q, k, v, dout, mask_fn: MaskFn, scale: float, n_rows: int, piece: int = PIECE,
                        threads: Optional[int] = None):
     """LSE [H_q, N] and delta [H_q, N] (delta = <dO, O> of the oracle's O) of every row."""

@@ -2,7 +2,10 @@
 bench.py times (every head, every clean shard, merge, backward per shard).
 
 KV-head group 0 (q-heads 0..G-1, KV head 0) is compared with the fp64 oracle
-element by element:
+element by element.  At the 256K rank share (sharded) and the varlen workload
+that is every element of the group: all rows' O, LSE and dQ and all keys' dK
+and dV (tests/fullsize_ref.group_reference, about 10^10 score elements each, a
+minute or two on the host's cores).  Elsewhere:
   * sampled query rows (1024; 4096 at the 1M rank share): O, LSE and dQ, each
     row exact on its own (tests/fullsize_ref.py composes the oracle over key
     pieces with the exact LSE merge);
@@ -72,9 +75,10 @@ def check_sum_identities(dk, dv, dout, G, label):
     log(f"{label}: gradient-sum identities hold on every KV head (last: dV {rel:.1e}, dK {relk:.1e})")
 
 
-def check_keys(name, got, want):
+def check_keys(name, got, want, per_key_bound=True):
     """Element-wise dK or dV of a set of keys: the stated tensor bounds, a per-key
-    relative bound, and exact zeros where the reference is exactly zero."""
+    relative bound (or, with per_key_bound=False, its worst value printed only),
+    and exact zeros where the reference is exactly zero."""
     got = got.double().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     zero = np.all(want == 0, axis=1)
@@ -86,7 +90,8 @@ def check_keys(name, got, want):
     worst = int(np.argmax(per))
     print(f"  {name}: {int(nz.sum())} keys, per-key relative L2 max {per.max():.2e} (key #{worst}), "
           f"median {np.median(per):.2e}; {int(zero.sum())} exact zeros", flush=True)
-    assert per.max() <= TOL_PER_KEY, f"{name}: key #{worst} relative error {per.max():.2e}"
+    if per_key_bound:
+        assert per.max() <= TOL_PER_KEY, f"{name}: key #{worst} relative error {per.max():.2e}"
 
 
 def check_rows(label, view, rows, o, lse, dq):
@@ -99,7 +104,22 @@ def check_rows(label, view, rows, o, lse, dq):
     check_close("dq[rows]", dq[r, :G], dq_r)
 
 
-def run_bdlm_fullsize(idx, n_rows, fused=False):
+def check_every_element(label, view, o, lse, dq, dk, dv):
+    """Every output of KV-head group 0 (q-heads 0..G-1, KV head 0) against the oracle."""
+    G = view["G"]
+    t0 = time.time()
+    log(f"{label}: oracle on every row and key of KV-head group 0 "
+        f"({view['q'].shape[0]} rows x {G} q-heads, {view['k'].shape[0]} keys)")
+    O, L, DQ, DK, DV = fr.group_reference(view["q"], view["k"], view["v"], view["dout"], view["mask"], view["scale"])
+    log(f"{label}: reference done in {time.time() - t0:.0f} s")
+    check_lse("lse[group 0, every row]", lse[:G], L)
+    check_close("o[group 0, every row]", o[:, :G], O)
+    check_close("dq[group 0, every row]", dq[:, :G], DQ)
+    check_keys("dk[kv head 0, every key]", dk[:, 0], DK[:, 0], per_key_bound=False)
+    check_keys("dv[kv head 0, every key]", dv[:, 0], DV[:, 0], per_key_bound=False)
+
+
+def run_bdlm_fullsize(idx, n_rows, fused=False, every_element=False):
     need_gpu()
     cfg = wl.config(idx)
     p = cfg.problem
@@ -136,13 +156,18 @@ def run_bdlm_fullsize(idx, n_rows, fused=False):
     check_keys("dk[corrupted self-block keys]", dk[keys[~clean], 0], fx["dk"][~clean])
     check_keys("dv[corrupted self-block keys]", dv[keys[~clean], 0], fx["dv"][~clean])
 
+    if every_element:
+        check_every_element(cfg.name, view, o, lse, dq, dk, dv)
+        return
     rng = np.random.default_rng(idx)
     rows = np.sort(rng.choice(p.n_q, n_rows, replace=False))
     check_rows(cfg.name, view, rows, o, lse, dq)
 
 
 def test_csbp_256k_rank_share_fullsize():
-    run_bdlm_fullsize(3, n_rows=1024)
+    """The headline workload: every element of KV-head group 0 (all 32768 rows x 4
+    q-heads and all 278528 keys of KV head 0), plus the stored spread keys."""
+    run_bdlm_fullsize(3, n_rows=1024, every_element=True)
 
 
 def test_csbp_256k_rank_share_fused_fullsize():
@@ -187,9 +212,7 @@ def test_varlen_262k_fullsize():
         f"({int(((keys >= cu[longest]) & (keys < cu[longest + 1])).sum())} in the longest document)")
     check_keys("dk[keys]", dk[keys, 0], fx["dk"])
     check_keys("dv[keys]", dv[keys, 0], fx["dv"])
-    rng = np.random.default_rng(4)
-    rows = np.sort(rng.choice(cfg.total, 1024, replace=False))
-    check_rows(cfg.name, view, rows, o, lse, dq)
+    check_every_element(cfg.name, view, o, lse, dq, dk, dv)
 
 
 def test_cad_tasks_262k_fullsize():
