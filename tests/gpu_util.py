@@ -10,10 +10,11 @@ import oracle
 from masked_long_context_amd import workloads as wl
 from masked_long_context_amd.rank_step import BdlmRankStep, TaskStep, VarlenStep
 
-# bf16 outputs O, dQ, dK, dV: max abs error and relative L2 error; fp32 LSE: max abs error.
-# The max-abs bound applies to each element's error beyond the bf16 rounding of its
-# exact value: a correctly rounded bf16 number is up to |x| 2^-9 away from x, which
-# exceeds 2e-2 once |x| >= 8, so no bf16 output could meet a plain 2e-2 there.
+# bf16 outputs O, dQ, dK, dV: every element within TOL_MAX_ABS + TOL_REL_L2 |x| of the
+# oracle's x (an absolute and a relative tolerance combined per element, as
+# numpy.allclose does: a plain absolute 2e-2 cannot hold for large |x| in bf16, whose
+# correct rounding alone is up to |x| 2^-9 away, 3e-2 at |x| = 9.6), and the
+# tensor's relative L2 error within TOL_REL_L2; fp32 LSE: max abs error.
 TOL_MAX_ABS = 2e-2
 TOL_REL_L2 = 5e-3
 TOL_LSE = 1e-5
@@ -41,12 +42,16 @@ def check_close(name, got, want, max_abs=TOL_MAX_ABS, rel=TOL_REL_L2):
     ma = float(np.abs(diff).max())
     nrm = float(np.linalg.norm(want))
     rl = float(np.linalg.norm(diff) / nrm) if nrm > 0 else float(np.linalg.norm(diff))
-    rounding = np.abs(torch.from_numpy(want).to(torch.bfloat16).double().numpy() - want)
-    floor = float(rounding.max())
-    beyond = float((np.abs(diff) - rounding).max())     # error beyond the output format's rounding
-    print(f"  {name}: max_abs={ma:.3e} (beyond bf16 rounding: {beyond:.3e}) rel_l2={rl:.3e} "
-          f"(|ref|max={np.abs(want).max():.3e}, bf16 rounding of ref alone: {floor:.3e})", flush=True)
-    assert beyond <= max_abs, f"{name}: max abs error beyond bf16 rounding {beyond:.3e} > {max_abs}"
+    floor = float(np.abs(torch.from_numpy(want).to(torch.bfloat16).double().numpy() - want).max())
+    # each element against max_abs + rel |x|: the ratio must stay <= 1
+    ratio = np.abs(diff) / (max_abs + rel * np.abs(want))
+    worst = int(np.argmax(ratio))
+    r_max = float(ratio.reshape(-1)[worst])
+    print(f"  {name}: max_abs={ma:.3e} rel_l2={rl:.3e} element bound ratio={r_max:.3f} "
+          f"(at |ref|={np.abs(want).reshape(-1)[worst]:.3e}; |ref|max={np.abs(want).max():.3e}, "
+          f"bf16 rounding of ref alone: {floor:.3e})", flush=True)
+    assert r_max <= 1.0, (f"{name}: element error {np.abs(diff).reshape(-1)[worst]:.3e} above "
+                          f"{max_abs} + {rel} |ref| at |ref|={np.abs(want).reshape(-1)[worst]:.3e}")
     assert rl <= rel, f"{name}: relative L2 error {rl:.3e} > {rel}"
     return ma, rl
 
