@@ -436,7 +436,8 @@ def main():
                          "6 = workload 4's documents as core-attention tasks with prefix contexts; "
                          "7 = conventional context parallelism's share of the same 256K sequence")
     ap.add_argument("--fused", action="store_true",
-                    help="workloads 1-3, 5: pass the whole clean K/V as one range (all shards resident)")
+                    help="workloads 1-3, 5, 7: every clean shard resident, each in a buffer of its own, and "
+                         "one launch per kernel over all of them (no partials, no merge)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=1,
                     help="spread the independent per-shard calls over this many streams (workloads 1-3, 5, 7)")
@@ -458,7 +459,7 @@ def main():
 
     import torch
     from masked_long_context_amd import workloads as wl
-    from masked_long_context_amd.rank_step import BdlmRankStep
+    from masked_long_context_amd.rank_step import BdlmRankStep, ResidentShardsStep
 
     cfg = wl.config(args.config)
     if args.config in (4, 6):
@@ -468,23 +469,34 @@ def main():
     print(f"# bench: generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = wl.bdlm_inputs(cfg, seed=0)
     g = {k: v.cuda() for k, v in inp.items()}
-    # --fused: every clean K/V shard resident at once and passed as one range, so the
-    # forward writes O and LSE directly (no fp32 partials, no merge) and each
-    # backward kernel runs once over the whole range
-    shards = [(0, p.clean_len, True)] if args.fused else list(cfg.shards)
-    workload = cfg.name + ("_fused_whole_range" if args.fused else "")
+    # --fused: every clean K/V shard resident at once, each in a buffer of its own
+    # (as received), and one launch per kernel over all of them: the forward
+    # writes O and LSE directly (no fp32 partials, no merge)
+    shards = list(cfg.shards)
+    workload = cfg.name + ("_resident_shards_one_launch" if args.fused else "")
     # plan building (host only, once per problem; outside the timed step)
     from masked_long_context_amd import bdattn as B
     t_plan = time.perf_counter()
-    for (o_, n_, loc) in shards:
-        B.Plan.from_problem(p.with_kv(o_, n_, loc))
+    if args.fused:
+        B.Plan.from_problem(p.with_kv(0, p.clean_len, True))
+    else:
+        for (o_, n_, loc) in shards:
+            B.Plan.from_problem(p.with_kv(o_, n_, loc))
     plan_ms = (time.perf_counter() - t_plan) * 1e3
-    step = BdlmRankStep(p, shards, streams=args.streams)
+    if args.fused:
+        step = ResidentShardsStep(p, shards)
+        k_sh = [g["k_clean"][o_:o_ + n_].clone() for (o_, n_, _) in shards]
+        v_sh = [g["v_clean"][o_:o_ + n_].clone() for (o_, n_, _) in shards]
+        args_ = (g["q"], k_sh, v_sh, g["k_corr"], g["v_corr"], g["dout"])
+        n_launch, n_act = 1, 0
+    else:
+        step = BdlmRankStep(p, shards, streams=args.streams)
+        args_ = (g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+        n_launch, n_act = len(shards), len(step.active)
     timer = EventTimer()
     step.timer = timer
     pairs = step.useful_pairs
     flops = pairs * p.h_q * 14 * p.head_dim
-    args_ = (g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
     print(f"# bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step.step(*args_)
@@ -505,7 +517,6 @@ def main():
 
     # per-kernel rates from the events around each library call (one kernel per call)
     n_sh = len(shards)
-    n_act = len(step.active)
     per = {}
     for tag, dflops in (("fwd", 4), ("dkdv", 8), ("dq", 6)):
         tms, tn = tot.get(tag, (0.0, 1))
@@ -514,11 +525,11 @@ def main():
                         tflops=pairs * p.h_q * dflops * p.head_dim * args.steps / (tms * 1e-3) / 1e12 if tms else 0.0)
     # dominant kernel: the key-major dK/dV kernel (8d flops per useful pair and q-head)
     dk = per["dkdv"]
-    dk_flops_per_launch = pairs * p.h_q * 8 * p.head_dim / n_sh
+    dk_flops_per_launch = pairs * p.h_q * 8 * p.head_dim / n_launch
     dk_achieved = dk_flops_per_launch / (dk["ms_per_launch"] * 1e-3) / 1e12
     # algorithmic HBM bytes of one dK/dV launch, averaged over the launches: Q and dO
     # of every query row, the range's K and V read and dK and dV written, LSE and delta
-    kv_rows = sum(n + (p.n_corr if loc else 0) for (_, n, loc) in shards) / n_sh
+    kv_rows = sum(n + (p.n_corr if loc else 0) for (_, n, loc) in shards) / n_launch
     dk_alg_bytes = int(2 * p.n_q * p.h_q * p.head_dim * 2 + 4 * kv_rows * p.h_kv * p.head_dim * 2
                        + 2 * p.h_q * p.n_q * 4)
     merge_ms, merge_n = tot.get("merge", (0.0, 1))
@@ -560,7 +571,7 @@ def main():
 
     metric = METRIC if args.config == 3 else f"BDLM attention fwd+bwd useful-pair TFLOP/s and % bf16 MFMA peak, {cfg.name}"
     if args.fused:
-        metric += " (all clean K/V resident, one fused range)"
+        metric += " (all clean shards resident, one launch per kernel)"
     if args.graph:
         metric += " (step replayed from a HIP graph)"
     out = {
@@ -616,8 +627,12 @@ def main():
     if not args.no_cpu_baseline:
         print("# bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"], ref = cpu_baseline(cfg, inp, pairs)
-        out["parity"] = parity_report(ref, step.o, step.lse, step.dq, torch.cat([step.dk_clean, step.dk_corr]),
-                                      torch.cat([step.dv_clean, step.dv_corr]))
+        dk_c = torch.cat(step.dk_shards) if args.fused else step.dk_clean
+        dv_c = torch.cat(step.dv_shards) if args.fused else step.dv_clean
+        corr = [step.dk_corr] if step.dk_corr is not None else []
+        corv = [step.dv_corr] if step.dv_corr is not None else []
+        out["parity"] = parity_report(ref, step.o, step.lse, step.dq, torch.cat([dk_c] + corr),
+                                      torch.cat([dv_c] + corv))
     print(json.dumps(out), flush=True)
 
 

@@ -81,6 +81,11 @@ typedef enum {
 
 typedef enum { BDATTN_BF16 = 0, BDATTN_F32 = 1 } bdattn_dtype;
 
+/* Most buffers a clean K/V range may be split over (bdattn_kv_shards), and the
+ * multiple of positions each buffer but the last must hold. */
+#define BDATTN_MAX_SHARDS 16
+#define BDATTN_SHARD_ALIGN 128
+
 /* One rank's BDLM problem against ONE clean K/V range. */
 typedef struct {
   int64_t clean_len;          /* L: whole clean sequence length, multiple of block_size       */
@@ -291,6 +296,55 @@ int bdattn_bwd_dq(const bdattn_plan *plan, const void *q, const void *k_clean, c
                   const void *k_corr, const void *v_corr, const void *dout, const float *lse,
                   const float *delta, float *dq_accum, void *workspace, int64_t workspace_bytes,
                   void *stream);
+
+/* Every resident clean shard in one launch per kernel.
+ * Source: the block-parallelism abstract (the clean sequence is sharded by
+ * position, and a rank attends the clean K/V of the blocks before its own) and
+ * the rit.work explainer of CSBP, section on why conventional context
+ * parallelism sends extra data (what a rank receives is clean K/V).  When the
+ * shards a rank attends are all resident, each in the buffer it arrived in,
+ * per-range partials and their merge are not needed: one online-softmax pass
+ * over all of them merges them exactly in registers (the log-sum-exp identity
+ * of bdattn_lse_merge, applied key tile by key tile), and no fp32 partial
+ * leaves the chip.
+ * The plan covers the whole range of the shards (kv_clean_offset: the first
+ * shard's first position; kv_clean_len: the sum of their lengths).  Buffer i
+ * holds positions [i shard_len, (i + 1) shard_len) of that range, the last one
+ * the rest: 1 <= n_shards <= BDATTN_MAX_SHARDS; for n_shards > 1, shard_len is a
+ * multiple of BDATTN_SHARD_ALIGN and every buffer holds at least one position,
+ * (n_shards - 1) shard_len < kv_clean_len <= n_shards shard_len (n_shards = 1:
+ * shard_len is ignored).  k[i], v[i]: [len_i][h_kv][head_dim] bf16, len_i the
+ * buffer's positions; dk[i], dv[i] (backward only, else ignored): the same
+ * shapes, written with `=`, zeros for keys no query attends.  The struct is
+ * read on the host during the call.  Any plan (a varlen plan: its packed K/V
+ * split the same way, NULL corrupted pointers).
+ * Results are bit for bit those of bdattn_fwd / bdattn_bwd (or the varlen
+ * calls) with the range in one buffer.  Errors: as bdattn_fwd / bdattn_bwd;
+ * EINVAL also for kv NULL, n_shards out of range, or buffers that do not cover
+ * the range as above; EALIGN for shard_len not a multiple of BDATTN_SHARD_ALIGN. */
+typedef struct bdattn_kv_shards {
+  int32_t n_shards;
+  int64_t shard_len;
+  const void *k[BDATTN_MAX_SHARDS];
+  const void *v[BDATTN_MAX_SHARDS];
+  void *dk[BDATTN_MAX_SHARDS];
+  void *dv[BDATTN_MAX_SHARDS];
+} bdattn_kv_shards;
+
+int bdattn_fwd_shards(const bdattn_plan *plan, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                      const void *v_corr, void *o, int32_t o_dtype, float *lse, void *workspace,
+                      int64_t workspace_bytes, void *stream);
+int bdattn_bwd_shards(const bdattn_plan *plan, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                      const void *v_corr, const void *dout, const float *lse, const float *delta,
+                      float *dq_accum, void *dk_corr, void *dv_corr, void *workspace, int64_t workspace_bytes,
+                      void *stream);
+int bdattn_bwd_dkdv_shards(const bdattn_plan *plan, const void *q, const bdattn_kv_shards *kv,
+                           const void *k_corr, const void *v_corr, const void *dout, const float *lse,
+                           const float *delta, void *dk_corr, void *dv_corr, void *workspace,
+                           int64_t workspace_bytes, void *stream);
+int bdattn_bwd_dq_shards(const bdattn_plan *plan, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                         const void *v_corr, const void *dout, const float *lse, const float *delta,
+                         float *dq_accum, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* dq (bf16) = dq_accum (fp32), n_elems elements (round to nearest even). */
 int bdattn_dq_finalize(const float *dq_accum, void *dq, int64_t n_elems, void *stream);

@@ -44,6 +44,16 @@ class Problem(ctypes.Structure):
                 ("h_q", c_int32), ("h_kv", c_int32), ("head_dim", c_int32), ("softmax_scale", c_float)]
 
 
+MAX_SHARDS, SHARD_ALIGN = 16, 128
+
+
+class KvShards(ctypes.Structure):
+    """Mirror of bdattn_kv_shards: the clean K/V range (and its gradients) split
+    over several buffers."""
+    _fields_ = [("n_shards", c_int32), ("shard_len", c_int64), ("k", c_void_p * MAX_SHARDS),
+                ("v", c_void_p * MAX_SHARDS), ("dk", c_void_p * MAX_SHARDS), ("dv", c_void_p * MAX_SHARDS)]
+
+
 _LIB = None
 
 _SIGS = {
@@ -76,6 +86,14 @@ _SIGS = {
     "bdattn_cast_f32_bf16": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_fwd": (c_int32, [c_void_p] * 5 + [c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_varlen_bwd": (c_int32, [c_void_p] * 11 + [c_int64, c_void_p]),
+    "bdattn_fwd_shards": (c_int32, [c_void_p, c_void_p, ctypes.POINTER(KvShards), c_void_p, c_void_p, c_void_p,
+                                    c_int32, c_void_p, c_void_p, c_int64, c_void_p]),
+    "bdattn_bwd_shards": (c_int32, [c_void_p, c_void_p, ctypes.POINTER(KvShards)] + [c_void_p] * 9
+                          + [c_int64, c_void_p]),
+    "bdattn_bwd_dkdv_shards": (c_int32, [c_void_p, c_void_p, ctypes.POINTER(KvShards)] + [c_void_p] * 8
+                               + [c_int64, c_void_p]),
+    "bdattn_bwd_dq_shards": (c_int32, [c_void_p, c_void_p, ctypes.POINTER(KvShards)] + [c_void_p] * 7
+                             + [c_int64, c_void_p]),
     "bdattn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -333,6 +351,55 @@ def _grad_kv_args(plan, dev, dk0, dv0, dk1, dv1):
     return None, None
 
 
+def shard_split(n_keys: int, n_shards: int, shard_len: int):
+    """Lengths of the buffers of a range of n_keys positions split over n_shards
+    buffers of shard_len positions (the last holds the rest), or an error."""
+    if not 1 <= n_shards <= MAX_SHARDS:
+        raise BdattnError(EINVAL, f"{n_shards} shard buffers; 1 .. {MAX_SHARDS} are allowed")
+    if n_shards == 1:
+        return [n_keys]
+    if shard_len <= 0 or shard_len % SHARD_ALIGN:
+        raise BdattnError(EALIGN, f"shard length {shard_len} is not a positive multiple of {SHARD_ALIGN}")
+    if not (n_shards - 1) * shard_len < n_keys <= n_shards * shard_len:
+        raise BdattnError(EINVAL, f"{n_shards} buffers of {shard_len} positions do not cover {n_keys} positions "
+                                  "with at least one position in each")
+    return [shard_len] * (n_shards - 1) + [n_keys - (n_shards - 1) * shard_len]
+
+
+def make_shards(k_shards, v_shards, dk_shards=None, dv_shards=None) -> KvShards:
+    """The bdattn_kv_shards struct of lists of per-buffer tensors (no checks)."""
+    kv = KvShards()
+    kv.n_shards = len(k_shards)
+    kv.shard_len = int(k_shards[0].shape[0]) if len(k_shards) > 1 else 0
+    for i in range(len(k_shards)):
+        kv.k[i] = k_shards[i].data_ptr()
+        kv.v[i] = v_shards[i].data_ptr()
+        if dk_shards is not None:
+            kv.dk[i] = dk_shards[i].data_ptr()
+            kv.dv[i] = dv_shards[i].data_ptr()
+    return kv
+
+
+def _shard_args(plan, dev, k_shards, v_shards, dk_shards=None, dv_shards=None) -> KvShards:
+    """Check per-buffer K/V (and dK/dV) lists against the plan's clean range."""
+    k_shards, v_shards = list(k_shards), list(v_shards)
+    if len(v_shards) != len(k_shards) or not k_shards:
+        raise BdattnError(EINVAL, "k_shards and v_shards must be non-empty lists of the same length")
+    lens = shard_split(plan.n_kv(0), len(k_shards), int(k_shards[0].shape[0]) if len(k_shards) > 1 else 0)
+    _, h_kv, d = plan.kv_shape(0)
+    b = _bf16()
+    lists = [("k", k_shards), ("v", v_shards)]
+    if dk_shards is not None or dv_shards is not None:
+        dk_shards, dv_shards = list(dk_shards or []), list(dv_shards or [])
+        if len(dk_shards) != len(k_shards) or len(dv_shards) != len(k_shards):
+            raise BdattnError(EINVAL, "dk_shards and dv_shards must hold one tensor per K/V buffer")
+        lists += [("dk", dk_shards), ("dv", dv_shards)]
+    for nm, ts in lists:
+        for i, t in enumerate(ts):
+            _want(t, f"{nm}_shards[{i}]", (lens[i], h_kv, d), b, dev)
+    return make_shards(k_shards, v_shards, dk_shards, dv_shards)
+
+
 def _row_args(plan, dev, lse, delta=None, dout=None):
     _want(lse, "lse", plan.lse_shape(), _f32(), dev)
     if delta is not None:
@@ -445,6 +512,72 @@ def bdattn_bwd_dq(plan: Plan, q, k_clean, v_clean, k_corr, v_corr, dout, lse, de
                                _stream(stream)))
 
 
+def _corr_args(plan, dev, k_corr, v_corr, g="k_corr"):
+    if plan.n_kv(1) > 0:
+        for t, nm in ((k_corr, g), (v_corr, g.replace("k", "v", 1))):
+            _want(t, nm, plan.kv_shape(1), _bf16(), dev)
+        return k_corr, v_corr
+    return None, None
+
+
+def bdattn_fwd_shards(plan: Plan, q, k_shards, v_shards, k_corr, v_corr, o, lse, ws, stream=None):
+    """bdattn_fwd over a clean range held in several buffers (lists of tensors)."""
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    kv = _shard_args(plan, dev, k_shards, v_shards)
+    k_corr, v_corr = _corr_args(plan, dev, k_corr, v_corr)
+    _want(o, "o", plan.q_shape(), _bf16_or_f32(), dev)
+    _row_args(plan, dev, lse=lse)
+    _want_ws(ws, plan, dev)
+    _on_one_gpu(dev, stream)
+    _check(lib().bdattn_fwd_shards(plan.handle, _ptr(q), ctypes.byref(kv), _ptr(k_corr), _ptr(v_corr), _ptr(o),
+                                   _dtype_code(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _bwd_shards_common(plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta, ws, dk_shards, dv_shards):
+    dev = []
+    _want(q, "q", plan.q_shape(), _bf16(), dev)
+    kv = _shard_args(plan, dev, k_shards, v_shards, dk_shards, dv_shards)
+    k_corr, v_corr = _corr_args(plan, dev, k_corr, v_corr)
+    _row_args(plan, dev, lse=lse, delta=delta, dout=dout)
+    _want_ws(ws, plan, dev)
+    return dev, kv, k_corr, v_corr
+
+
+def bdattn_bwd_shards(plan: Plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta, dq_accum,
+                      dk_shards, dv_shards, dk_corr, dv_corr, ws, stream=None):
+    dev, kv, k_corr, v_corr = _bwd_shards_common(plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta,
+                                                 ws, dk_shards, dv_shards)
+    _want(dq_accum, "dq_accum", plan.q_shape(), _f32(), dev)
+    dk_corr, dv_corr = _corr_args(plan, dev, dk_corr, dv_corr, g="dk_corr")
+    _on_one_gpu(dev, stream)
+    _check(lib().bdattn_bwd_shards(plan.handle, _ptr(q), ctypes.byref(kv), _ptr(k_corr), _ptr(v_corr), _ptr(dout),
+                                   _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(dk_corr), _ptr(dv_corr), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+
+
+def bdattn_bwd_dkdv_shards(plan: Plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta,
+                           dk_shards, dv_shards, dk_corr, dv_corr, ws, stream=None):
+    dev, kv, k_corr, v_corr = _bwd_shards_common(plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta,
+                                                 ws, dk_shards, dv_shards)
+    dk_corr, dv_corr = _corr_args(plan, dev, dk_corr, dv_corr, g="dk_corr")
+    _on_one_gpu(dev, stream)
+    _check(lib().bdattn_bwd_dkdv_shards(plan.handle, _ptr(q), ctypes.byref(kv), _ptr(k_corr), _ptr(v_corr),
+                                        _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dk_corr), _ptr(dv_corr), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
+
+
+def bdattn_bwd_dq_shards(plan: Plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta, dq_accum, ws,
+                         stream=None):
+    dev, kv, k_corr, v_corr = _bwd_shards_common(plan, q, k_shards, v_shards, k_corr, v_corr, dout, lse, delta,
+                                                 ws, None, None)
+    _want(dq_accum, "dq_accum", plan.q_shape(), _f32(), dev)
+    _on_one_gpu(dev, stream)
+    _check(lib().bdattn_bwd_dq_shards(plan.handle, _ptr(q), ctypes.byref(kv), _ptr(k_corr), _ptr(v_corr),
+                                      _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_accum), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
+
+
 def bdattn_varlen_bwd(plan: Plan, q, k, v, dout, lse, delta, dq_accum, dk, dv, ws, stream=None):
     dev = []
     _want(q, "q", plan.q_shape(), _bf16(), dev)
@@ -528,6 +661,21 @@ def bwd_dkdv_unchecked(plan, q, kc, vc, kx, vx, dout, lse, delta, dkc, dvc, dkx,
 def bwd_dq_unchecked(plan, q, kc, vc, kx, vx, dout, lse, delta, dq_accum, ws, stream):
     _check(lib().bdattn_bwd_dq(plan.handle, _p(q), _p(kc), _p(vc), _p(kx), _p(vx), _p(dout), _p(lse), _p(delta),
                                _p(dq_accum), _p(ws), ws.numel(), stream))
+
+
+def fwd_shards_unchecked(plan, q, kv: KvShards, kx, vx, o, lse, ws, stream):
+    _check(lib().bdattn_fwd_shards(plan.handle, _p(q), ctypes.byref(kv), _p(kx), _p(vx), _p(o), _dtype_code(o),
+                                   _p(lse), _p(ws), ws.numel(), stream))
+
+
+def bwd_dkdv_shards_unchecked(plan, q, kv: KvShards, kx, vx, dout, lse, delta, dkx, dvx, ws, stream):
+    _check(lib().bdattn_bwd_dkdv_shards(plan.handle, _p(q), ctypes.byref(kv), _p(kx), _p(vx), _p(dout), _p(lse),
+                                        _p(delta), _p(dkx), _p(dvx), _p(ws), ws.numel(), stream))
+
+
+def bwd_dq_shards_unchecked(plan, q, kv: KvShards, kx, vx, dout, lse, delta, dq_accum, ws, stream):
+    _check(lib().bdattn_bwd_dq_shards(plan.handle, _p(q), ctypes.byref(kv), _p(kx), _p(vx), _p(dout), _p(lse),
+                                      _p(delta), _p(dq_accum), _p(ws), ws.numel(), stream))
 
 
 def cast_unchecked(src, dst, stream):

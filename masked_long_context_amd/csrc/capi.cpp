@@ -80,6 +80,56 @@ int check_ws(const bdattn::Plan &p, const void *ws, int64_t bytes) {
   return BDATTN_OK;
 }
 
+bdattn_kv_shards one_buffer(const void *k, const void *v, void *dk = nullptr, void *dv = nullptr) {
+  bdattn_kv_shards kv{};
+  kv.n_shards = 1;
+  kv.k[0] = k;
+  kv.v[0] = v;
+  kv.dk[0] = dk;
+  kv.dv[0] = dv;
+  return kv;
+}
+
+// The clean segment's buffers against the plan: count, split and pointers (K/V
+// when the segment has keys, dK/dV too when `grads`).
+int check_shards(const bdattn::Plan &p, const bdattn_kv_shards *kv, bool grads) {
+  if (!kv) return fail(BDATTN_EINVAL, "kv shards is NULL");
+  const int n = kv->n_shards;
+  if (n < 1 || n > BDATTN_MAX_SHARDS) return fail(BDATTN_EINVAL, "n_shards must be in 1 .. BDATTN_MAX_SHARDS");
+  const int64_t n0 = p.n_seg[0];
+  if (n > 1) {
+    if (kv->shard_len <= 0 || kv->shard_len % BDATTN_SHARD_ALIGN != 0)
+      return fail(BDATTN_EALIGN, "shard_len must be a positive multiple of BDATTN_SHARD_ALIGN");
+    // shard_len < n0 < 2^31 first, so that the products below cannot overflow
+    if (!(kv->shard_len < n0 && (n - 1) * kv->shard_len < n0 && n0 <= n * kv->shard_len))
+      return fail(BDATTN_EINVAL, "the shard buffers must cover the plan's clean range, each holding at least one "
+                                 "position: (n_shards - 1) shard_len < kv_clean_len <= n_shards shard_len");
+  }
+  for (int i = 0; i < n; ++i) {
+    const std::string ix = "[" + std::to_string(i) + "]";
+    int rc = check_ptr(kv->k[i], ("kv.k" + ix).c_str(), n0 > 0);
+    if (rc == BDATTN_OK) rc = check_ptr(kv->v[i], ("kv.v" + ix).c_str(), n0 > 0);
+    if (rc == BDATTN_OK) rc = check_ptr(kv->dk[i], ("kv.dk" + ix).c_str(), n0 > 0 && grads);
+    if (rc == BDATTN_OK) rc = check_ptr(kv->dv[i], ("kv.dv" + ix).c_str(), n0 > 0 && grads);
+    if (rc != BDATTN_OK) return rc;
+  }
+  return BDATTN_OK;
+}
+
+void fill_shards(const bdattn_kv_shards &kv, bdattn::KvShardTable &t, bdattn::GradShardTable *g) {
+  t = bdattn::KvShardTable{};
+  t.n = kv.n_shards;
+  t.len = kv.n_shards > 1 ? (int32_t)kv.shard_len : 0;
+  for (int i = 0; i < kv.n_shards; ++i) {
+    t.k[i] = kv.k[i];
+    t.v[i] = kv.v[i];
+    if (g) {
+      g->dk[i] = kv.dk[i];
+      g->dv[i] = kv.dv[i];
+    }
+  }
+}
+
 // Copies the plan's tables into the head of `dst` on `stream`.
 int upload(bdattn_plan *pl, void *dst, hipStream_t stream) {
   bdattn::Plan &p = pl->p;
@@ -106,8 +156,8 @@ const int32_t *img(const void *base, int64_t off) {
 namespace bdattn {
 namespace abi {
 
-int check_fwd_args(const bdattn_plan *pl, const void *q, const void *k0, const void *v0, const void *k1,
-                   const void *v1, const void *o, int32_t o_dtype, const float *lse) {
+int check_fwd_shards(const bdattn_plan *pl, const void *q, const bdattn_kv_shards *kv, const void *k1,
+                     const void *v1, const void *o, int32_t o_dtype, const float *lse) {
   if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
   const bdattn::Plan &p = pl->p;
   CHECK(o_dtype == BDATTN_BF16 || o_dtype == BDATTN_F32, BDATTN_EUNSUPPORTED, "o_dtype must be BF16 or F32");
@@ -115,21 +165,28 @@ int check_fwd_args(const bdattn_plan *pl, const void *q, const void *k0, const v
   CHECK_PTR(q, rows);
   CHECK_PTR(o, rows);
   CHECK_PTR(lse, rows);
-  CHECK_PTR(k0, p.n_seg[0] > 0);
-  CHECK_PTR(v0, p.n_seg[0] > 0);
+  int rc = check_shards(p, kv, false);
+  if (rc != BDATTN_OK) return rc;
   CHECK_PTR(k1, p.n_seg[1] > 0);
   CHECK_PTR(v1, p.n_seg[1] > 0);
   return BDATTN_OK;
 }
 
-int launch_fwd_on_tables(const bdattn_plan *pl, const void *tables, const void *q, const void *k0, const void *v0,
-                         const void *k1, const void *v1, void *o, int32_t o_dtype, float *lse, hipStream_t s) {
+int check_fwd_args(const bdattn_plan *pl, const void *q, const void *k0, const void *v0, const void *k1,
+                   const void *v1, const void *o, int32_t o_dtype, const float *lse) {
+  const bdattn_kv_shards kv = one_buffer(k0, v0);
+  return check_fwd_shards(pl, q, &kv, k1, v1, o, o_dtype, lse);
+}
+
+int launch_fwd_shards(const bdattn_plan *pl, const void *tables, const void *q, const bdattn_kv_shards &kv,
+                      const void *k1, const void *v1, void *o, int32_t o_dtype, float *lse, hipStream_t s) {
   const bdattn::Plan &p = pl->p;
   const void *ws = tables;
   bdattn::FwdArgs a{};
-  a.k[0] = k0;
+  fill_shards(kv, a.sh, nullptr);
+  a.k[0] = kv.k[0];
   a.k[1] = k1;
-  a.v[0] = v0;
+  a.v[0] = kv.v[0];
   a.v[1] = v1;
   a.n_seg[0] = (int32_t)p.n_seg[0];
   a.n_seg[1] = (int32_t)p.n_seg[1];
@@ -149,6 +206,11 @@ int launch_fwd_on_tables(const bdattn_plan *pl, const void *tables, const void *
   return BDATTN_OK;
 }
 
+int launch_fwd_on_tables(const bdattn_plan *pl, const void *tables, const void *q, const void *k0, const void *v0,
+                         const void *k1, const void *v1, void *o, int32_t o_dtype, float *lse, hipStream_t s) {
+  return launch_fwd_shards(pl, tables, q, one_buffer(k0, v0), k1, v1, o, o_dtype, lse, s);
+}
+
 int64_t fwd_table_bytes(const bdattn_plan *pl) { return pl->p.hdr.off_bq; }
 
 }  // namespace abi
@@ -156,10 +218,10 @@ int64_t fwd_table_bytes(const bdattn_plan *pl) { return pl->p.hdr.off_bq; }
 
 namespace {
 
-int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
-            const void *v1, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
+int run_fwd(const bdattn_plan *cpl, const void *q, const bdattn_kv_shards *kv, const void *k1, const void *v1,
+            void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
   bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
-  int rc = bdattn::abi::check_fwd_args(pl, q, k0, v0, k1, v1, o, o_dtype, lse);
+  int rc = bdattn::abi::check_fwd_shards(pl, q, kv, k1, v1, o, o_dtype, lse);
   if (rc != BDATTN_OK) return rc;
   rc = check_ws(pl->p, ws, ws_bytes);
   if (rc != BDATTN_OK) return rc;
@@ -167,13 +229,18 @@ int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   hipStream_t s = (hipStream_t)stream;
   rc = upload(pl, ws, s);
   if (rc != BDATTN_OK) return rc;
-  return bdattn::abi::launch_fwd_on_tables(pl, ws, q, k0, v0, k1, v1, o, o_dtype, lse, s);
+  return bdattn::abi::launch_fwd_shards(pl, ws, q, *kv, k1, v1, o, o_dtype, lse, s);
 }
 
-int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
-            const void *v1, const void *dout, const float *lse, const float *delta, float *dq, void *dk0,
-            void *dv0, void *dk1, void *dv1, void *ws, int64_t ws_bytes, void *stream, bool do_dkdv = true,
-            bool do_dq = true) {
+int run_fwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
+            const void *v1, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes, void *stream) {
+  const bdattn_kv_shards kv = one_buffer(k0, v0);
+  return run_fwd(cpl, q, &kv, k1, v1, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int run_bwd(const bdattn_plan *cpl, const void *q, const bdattn_kv_shards *kv, const void *k1, const void *v1,
+            const void *dout, const float *lse, const float *delta, float *dq, void *dk1, void *dv1, void *ws,
+            int64_t ws_bytes, void *stream, bool do_dkdv = true, bool do_dq = true) {
   bdattn_plan *pl = const_cast<bdattn_plan *>(cpl);
   const bdattn::Plan &p = pl->p;
   const bool rows = p.n_q > 0;
@@ -184,28 +251,27 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
   CHECK_PTR(lse, work);
   CHECK_PTR(delta, work);
   CHECK_PTR(dq, work && do_dq);
-  CHECK_PTR(k0, p.n_seg[0] > 0);
-  CHECK_PTR(v0, p.n_seg[0] > 0);
-  CHECK_PTR(dk0, p.n_seg[0] > 0 && do_dkdv);
-  CHECK_PTR(dv0, p.n_seg[0] > 0 && do_dkdv);
+  int rc = check_shards(p, kv, do_dkdv);
+  if (rc != BDATTN_OK) return rc;
   CHECK_PTR(k1, p.n_seg[1] > 0);
   CHECK_PTR(v1, p.n_seg[1] > 0);
   CHECK_PTR(dk1, p.n_seg[1] > 0 && do_dkdv);
   CHECK_PTR(dv1, p.n_seg[1] > 0 && do_dkdv);
-  int rc = check_ws(p, ws, ws_bytes);
+  rc = check_ws(p, ws, ws_bytes);
   if (rc != BDATTN_OK) return rc;
   if (!any_keys) return BDATTN_OK;
   hipStream_t s = (hipStream_t)stream;
   rc = upload(pl, ws, s);
   if (rc != BDATTN_OK) return rc;
   bdattn::BwdArgs a{};
-  a.k[0] = k0;
+  fill_shards(*kv, a.sh, &a.gsh);
+  a.k[0] = kv->k[0];
   a.k[1] = k1;
-  a.v[0] = v0;
+  a.v[0] = kv->v[0];
   a.v[1] = v1;
-  a.dk[0] = dk0;
+  a.dk[0] = kv->dk[0];
   a.dk[1] = dk1;
-  a.dv[0] = dv0;
+  a.dv[0] = kv->dv[0];
   a.dv[1] = dv1;
   a.n_seg[0] = (int32_t)p.n_seg[0];
   a.n_seg[1] = (int32_t)p.n_seg[1];
@@ -234,6 +300,14 @@ int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v
     a.part[seg] = p.dkdv_split > 1 ? reinterpret_cast<float *>((char *)ws + p.off_part[seg]) : nullptr;
   HIP_CHECK(bdattn::launch_bwd(a, p.d, s, do_dkdv, do_dq), "backward kernels");
   return BDATTN_OK;
+}
+
+int run_bwd(const bdattn_plan *cpl, const void *q, const void *k0, const void *v0, const void *k1,
+            const void *v1, const void *dout, const float *lse, const float *delta, float *dq, void *dk0,
+            void *dv0, void *dk1, void *dv1, void *ws, int64_t ws_bytes, void *stream, bool do_dkdv = true,
+            bool do_dq = true) {
+  const bdattn_kv_shards kv = one_buffer(k0, v0, dk0, dv0);
+  return run_bwd(cpl, q, &kv, k1, v1, dout, lse, delta, dq, dk1, dv1, ws, ws_bytes, stream, do_dkdv, do_dq);
 }
 
 }  // namespace
@@ -422,6 +496,36 @@ int bdattn_varlen_bwd(const bdattn_plan *pl, const void *q, const void *k, const
   if (pl->p.kind != 1) return fail(BDATTN_EINVAL, "plan is not a varlen plan; use bdattn_bwd");
   return run_bwd(pl, q, k, v, nullptr, nullptr, dout, lse, delta, dq, dk, dv, nullptr, nullptr, ws, ws_bytes,
                  stream);
+}
+
+int bdattn_fwd_shards(const bdattn_plan *pl, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                      const void *v_corr, void *o, int32_t o_dtype, float *lse, void *ws, int64_t ws_bytes,
+                      void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  return run_fwd(pl, q, kv, k_corr, v_corr, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int bdattn_bwd_shards(const bdattn_plan *pl, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                      const void *v_corr, const void *dout, const float *lse, const float *delta, float *dq_accum,
+                      void *dk_corr, void *dv_corr, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  return run_bwd(pl, q, kv, k_corr, v_corr, dout, lse, delta, dq_accum, dk_corr, dv_corr, ws, ws_bytes, stream);
+}
+
+int bdattn_bwd_dkdv_shards(const bdattn_plan *pl, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                           const void *v_corr, const void *dout, const float *lse, const float *delta,
+                           void *dk_corr, void *dv_corr, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  return run_bwd(pl, q, kv, k_corr, v_corr, dout, lse, delta, nullptr, dk_corr, dv_corr, ws, ws_bytes, stream,
+                 true, false);
+}
+
+int bdattn_bwd_dq_shards(const bdattn_plan *pl, const void *q, const bdattn_kv_shards *kv, const void *k_corr,
+                         const void *v_corr, const void *dout, const float *lse, const float *delta,
+                         float *dq_accum, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  return run_bwd(pl, q, kv, k_corr, v_corr, dout, lse, delta, dq_accum, nullptr, nullptr, ws, ws_bytes, stream,
+                 false, true);
 }
 
 int bdattn_bwd_prepare(const bdattn_plan *pl, const void *o, int32_t o_dtype, const void *dout, float *delta,

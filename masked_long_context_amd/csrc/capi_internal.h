@@ -19,7 +19,10 @@ namespace abi {
 // Records the thread-local error text and returns `code`.
 int fail(int code, const std::string &msg);
 
-// Argument checks of the forward entry points (before any HIP call).
+// Argument checks of the forward entry points (before any HIP call): the clean
+// segment as a table of buffers, or in one buffer.
+int check_fwd_shards(const bdattn_plan *pl, const void *q, const bdattn_kv_shards *kv, const void *k1,
+                     const void *v1, const void *o, int32_t o_dtype, const float *lse);
 int check_fwd_args(const bdattn_plan *pl, const void *q, const void *k0, const void *v0, const void *k1,
                    const void *v1, const void *o, int32_t o_dtype, const float *lse);
 
@@ -27,6 +30,9 @@ int check_fwd_args(const bdattn_plan *pl, const void *q, const void *k0, const v
 // `tables` (laid out as the plan's image; only its forward prefix is read).
 int launch_fwd_on_tables(const bdattn_plan *pl, const void *tables, const void *q, const void *k0, const void *v0,
                          const void *k1, const void *v1, void *o, int32_t o_dtype, float *lse, hipStream_t s);
+
+int launch_fwd_shards(const bdattn_plan *pl, const void *tables, const void *q, const bdattn_kv_shards &kv,
+                      const void *k1, const void *v1, void *o, int32_t o_dtype, float *lse, hipStream_t s);
 
 // Bytes of the image prefix the forward kernel reads (header, row bounds, forward tiles).
 int64_t fwd_table_bytes(const bdattn_plan *pl);

@@ -65,7 +65,7 @@ struct DkdvLds {
 //            map); dS = P o (dP - delta), dK^T += Q(i)^T dS.
 // The roles share no data inside an iteration, so one barrier per iteration
 // suffices.
-template <int D, int KT, int ROLE>
+template <int D, int KT, int ROLE, bool SPLIT>
 __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int lb, int t0, int nt, int chunk,
                                           int kvh, int wave, int lane, const DkdvLds<D> &L) {
   constexpr int BM = BDATTN_BWD_BM;
@@ -82,12 +82,16 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
   }
   const int G = a.group;
 
+  // The buffer of this key tile (a key tile never straddles two) and the first
+  // key of that buffer.
+  const void *kbuf, *vbuf;
+  const int kbase = k0 - seg_buffer<SPLIT>(a, s, k0, kbuf, vbuf);
   // K (dV waves) or V (dK waves) as B operands (lane = key column, k = head dim).
   bf16x8 kvf[KT][NC];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const int64_t off = ((int64_t)(kvalid[kt] ? key[kt] : 0) * a.h_kv + kvh) * D;
-    const bf16 *src = (const bf16 *)(ROLE == 0 ? a.k[s] : a.v[s]) + off;
+    const int64_t off = ((int64_t)(kvalid[kt] ? key[kt] - kbase : 0) * a.h_kv + kvh) * D;
+    const bf16 *src = (const bf16 *)(ROLE == 0 ? kbuf : vbuf) + off;
 #pragma unroll
     for (int c = 0; c < NC; ++c) kvf[kt][c] = kvalid[kt] ? ld_bf16x8(src + 16 * c + 8 * g) : zero_bf16x8();
   }
@@ -383,10 +387,15 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs &a, int s, int k0, int l
     }
     return;
   }
+  // the gradient buffer of this tile, found again from the wave's first key (no
+  // register is kept live through the loop for it)
+  void *dkbuf, *dvbuf;
+  const int kw0 = SPLIT ? __builtin_amdgcn_readfirstlane(key[0]) : 0;
+  const int kbase_end = kw0 - grad_buffer<SPLIT>(a, s, kw0, dkbuf, dvbuf);
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     if (!kvalid[kt]) continue;
-    bf16 *outp = (bf16 *)(ROLE == 0 ? a.dv[s] : a.dk[s]) + ((int64_t)key[kt] * a.h_kv + kvh) * D;
+    bf16 *outp = (bf16 *)(ROLE == 0 ? dvbuf : dkbuf) + ((int64_t)(key[kt] - kbase_end) * a.h_kv + kvh) * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -406,7 +415,8 @@ constexpr int kDkdvKT = 1;
 constexpr int kDkdvThreads = 2 * (4 / kDkdvKT) * 64;
 static_assert(kDkdvThreads == BDATTN_DKDV_THREADS, "dK/dV workgroup size known to the scheduler");
 
-template <int D>
+// SPLIT: the clean segment sits in several buffers (a.sh, a.gsh).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kDkdvThreads, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int BM = BDATTN_BWD_BM;
   static_assert(BM == Tile<D>::ROWS, "query tile = one LDS tile");
@@ -432,15 +442,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void dkdv_kernel(BwdArgs a) {
   const int lb = ld_table(a.ktiles, (int64_t)kti * 4 + 2), le = ld_table(a.ktiles, (int64_t)kti * 4 + 3);
   const int total = (le - lb) * a.group;
   const int t0 = (int)((int64_t)total * chunk / a.split), t1 = (int)((int64_t)total * (chunk + 1) / a.split);
-  if (wave < 4 / kDkdvKT) dkdv_role<D, kDkdvKT, 0>(a, s, k0, lb, t0, t1 - t0, chunk, kvh, wave, lane, L);
-  else dkdv_role<D, kDkdvKT, 1>(a, s, k0, lb, t0, t1 - t0, chunk, kvh, wave, lane, L);
+  if (wave < 4 / kDkdvKT) dkdv_role<D, kDkdvKT, 0, SPLIT>(a, s, k0, lb, t0, t1 - t0, chunk, kvh, wave, lane, L);
+  else dkdv_role<D, kDkdvKT, 1, SPLIT>(a, s, k0, lb, t0, t1 - t0, chunk, kvh, wave, lane, L);
 }
 
 // Sum of the split dK/dV partials of one key segment, in chunk order (so the
 // result does not depend on scheduling), to bf16: n4 groups of 4 elements per
-// tensor, dK groups first, then dV.
-__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float *part, int split, int64_t n4, bf16 *dk,
-                                                          bf16 *dv) {
+// tensor, dK groups first, then dV.  The gradients go to n_buf buffers of
+// per_buf groups each (the last holds the rest).
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float *part, int split, int64_t n4,
+                                                          GradShardTable out, int n_buf, int64_t per_buf) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= 2 * n4) return;
   const int ro = i >= n4 ? 1 : 0;
@@ -451,10 +462,12 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float *part, int
   bf16x4 b;
 #pragma unroll
   for (int k = 0; k < 4; ++k) b[k] = (bf16)acc[k];
-  reinterpret_cast<bf16x4 *>(ro ? dv : dk)[e] = b;
+  const int bi = n_buf > 1 ? (int)min(e / per_buf, (int64_t)n_buf - 1) : 0;
+  reinterpret_cast<bf16x4 *>(ro ? out.dv[bi] : out.dk[bi])[e - bi * per_buf] = b;
 }
 
-template <int D>
+// SPLIT: the clean segment sits in several buffers (a.sh).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void dq_kernel(BwdArgs a) {
   constexpr int BN = BDATTN_FWD_BN;
   static_assert(BN == Tile<D>::ROWS, "key tile = one LDS tile");
@@ -516,10 +529,13 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void d
   auto issue = [&](int t, char *kd, char *vd) {
     const int s = t < nt[0] ? 0 : 1;
     const int k0 = s == 0 ? base[0] + t * BN : base[1] + (t - nt[0]) * BN;
-    const int64_t off = (int64_t)k0 * kv_stride + kvh * D;
+    // the buffer holding the key tile (a tile never straddles two)
+    const void *kbuf, *vbuf;
+    const int rb = seg_buffer<SPLIT>(a, s, k0, kbuf, vbuf);
+    const int64_t off = (int64_t)rb * kv_stride + kvh * D;
     const int nv = a.n_seg[s] - k0;
-    tile_load<D, BDATTN_FWD_WAVES>(kd, (const bf16 *)a.k[s] + off, kv_stride, nv, wave, lane);
-    tile_load<D, BDATTN_FWD_WAVES>(vd, (const bf16 *)a.v[s] + off, kv_stride, nv, wave, lane);
+    tile_load<D, BDATTN_FWD_WAVES>(kd, (const bf16 *)kbuf + off, kv_stride, nv, wave, lane);
+    tile_load<D, BDATTN_FWD_WAVES>(vd, (const bf16 *)vbuf + off, kv_stride, nv, wave, lane);
   };
   auto compute = [&](int t, const char *k_lds, const char *v_lds) {
     const int s = t < nt[0] ? 0 : 1;
@@ -608,16 +624,34 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void d
 hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, bool dq) {
   const int64_t kblocks = dkdv ? (int64_t)a.n_kt * a.h_kv * a.split : 0;
   if (kblocks > 0) {
-    if (d == 128) hipLaunchKernelGGL(dkdv_kernel<128>, dim3((unsigned)kblocks), dim3(kDkdvThreads), 0, s, a);
-    else hipLaunchKernelGGL(dkdv_kernel<64>, dim3((unsigned)kblocks), dim3(kDkdvThreads), 0, s, a);
+    const dim3 grid((unsigned)kblocks), block(kDkdvThreads);
+    const bool split = a.sh.n > 1;
+    if (d == 128) {
+      if (split) hipLaunchKernelGGL((dkdv_kernel<128, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((dkdv_kernel<128, false>), grid, block, 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((dkdv_kernel<64, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((dkdv_kernel<64, false>), grid, block, 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.split > 1) {
       for (int seg = 0; seg < 2; ++seg) {
         const int64_t n4 = (int64_t)a.n_seg[seg] * a.h_kv * d / 4;
         if (n4 == 0) continue;
+        GradShardTable out{};
+        int n_buf = 1;
+        int64_t per_buf = n4;
+        if (seg == 0) {
+          out = a.gsh;
+          n_buf = a.sh.n;
+          if (n_buf > 1) per_buf = (int64_t)a.sh.len * a.h_kv * d / 4;
+        } else {
+          out.dk[0] = a.dk[1];
+          out.dv[0] = a.dv[1];
+        }
         hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, s,
-                           (const float *)a.part[seg], a.split, n4, (bf16 *)a.dk[seg], (bf16 *)a.dv[seg]);
+                           (const float *)a.part[seg], a.split, n4, out, n_buf, per_buf);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
@@ -625,8 +659,15 @@ hipError_t launch_bwd(const BwdArgs &a, int32_t d, hipStream_t s, bool dkdv, boo
   }
   const int64_t qblocks = dq ? (int64_t)a.n_items * a.h_q : 0;
   if (qblocks > 0) {
-    if (d == 128) hipLaunchKernelGGL(dq_kernel<128>, dim3((unsigned)qblocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
-    else hipLaunchKernelGGL(dq_kernel<64>, dim3((unsigned)qblocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
+    const dim3 grid((unsigned)qblocks), block(64 * BDATTN_FWD_WAVES);
+    const bool split = a.sh.n > 1;
+    if (d == 128) {
+      if (split) hipLaunchKernelGGL((dq_kernel<128, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((dq_kernel<128, false>), grid, block, 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((dq_kernel<64, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((dq_kernel<64, false>), grid, block, 0, s, a);
+    }
   }
   return hipGetLastError();
 }

@@ -64,6 +64,36 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &c, int r0) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// K and V buffers holding row r (wave-uniform) of key segment s, and r's row in
+// them.  SPLIT: segment 0 sits in the buffers of a.sh; otherwise every segment
+// is one buffer (a.k[s], a.v[s]) and no lookup is made.
+template <bool SPLIT, class Args>
+__device__ __forceinline__ int seg_buffer(const Args &a, int s, int r, const void *&k, const void *&v) {
+  if (SPLIT && s == 0) {
+    const int i = min(r / a.sh.len, a.sh.n - 1);
+    k = a.sh.k[i];
+    v = a.sh.v[i];
+    return r - i * a.sh.len;
+  }
+  k = a.k[s];
+  v = a.v[s];
+  return r;
+}
+
+// The same for the dK and dV buffers (backward).
+template <bool SPLIT, class Args>
+__device__ __forceinline__ int grad_buffer(const Args &a, int s, int r, void *&dk, void *&dv) {
+  if (SPLIT && s == 0) {
+    const int i = min(r / a.sh.len, a.sh.n - 1);
+    dk = a.gsh.dk[i];
+    dv = a.gsh.dv[i];
+    return r - i * a.sh.len;
+  }
+  dk = a.dk[s];
+  dv = a.dv[s];
+  return r;
+}
+
 // Read of a table that no kernel writes while it runs, through the constant
 // address space: with a uniform address this becomes a scalar (SMEM) load,
 // which waits on lgkmcnt and so never stalls behind in-flight vector loads.

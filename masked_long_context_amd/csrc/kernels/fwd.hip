@@ -30,7 +30,8 @@ namespace {
 constexpr int kFwdTiles = BDATTN_FWD_STEP / 64;
 static_assert(kFwdTiles * 64 == BDATTN_FWD_STEP, "forward step = whole LDS tiles");
 
-template <int D>
+// SPLIT: the clean segment sits in several buffers (a.sh).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void fwd_kernel(FwdArgs a) {
   constexpr int KB = kFwdTiles;               // 64-row LDS tiles per key step
   constexpr int BN = KB * Tile<D>::ROWS;       // keys per step
@@ -98,9 +99,12 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
         r0 = a.n_seg[s] - 1;
         nv = 1;
       }
-      const int64_t off = (int64_t)r0 * kv_stride + kvh * D;
-      tile_load<D, BDATTN_FWD_WAVES>(kd + kb * TB, (const bf16 *)a.k[s] + off, kv_stride, nv, wave, lane);
-      tile_load<D, BDATTN_FWD_WAVES>(vd + kb * TB, (const bf16 *)a.v[s] + off, kv_stride, nv, wave, lane);
+      // the buffer holding the tile (a tile never straddles two)
+      const void *kbuf, *vbuf;
+      const int rb = seg_buffer<SPLIT>(a, s, r0, kbuf, vbuf);
+      const int64_t off = (int64_t)rb * kv_stride + kvh * D;
+      tile_load<D, BDATTN_FWD_WAVES>(kd + kb * TB, (const bf16 *)kbuf + off, kv_stride, nv, wave, lane);
+      tile_load<D, BDATTN_FWD_WAVES>(vd + kb * TB, (const bf16 *)vbuf + off, kv_stride, nv, wave, lane);
     }
   };
   auto compute = [&](int t, const char *kt_lds, const char *vt_lds) {
@@ -225,8 +229,15 @@ __global__ __launch_bounds__(64 * BDATTN_FWD_WAVES, 8 / BDATTN_FWD_WAVES) void f
 hipError_t launch_fwd(const FwdArgs &a, int32_t d, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_items * a.h_q;
   if (blocks == 0) return hipSuccess;
-  if (d == 128) hipLaunchKernelGGL(fwd_kernel<128>, dim3((unsigned)blocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
-  else hipLaunchKernelGGL(fwd_kernel<64>, dim3((unsigned)blocks), dim3(64 * BDATTN_FWD_WAVES), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(64 * BDATTN_FWD_WAVES);
+  const bool split = a.sh.n > 1;
+  if (d == 128) {
+    if (split) hipLaunchKernelGGL((fwd_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (split) hipLaunchKernelGGL((fwd_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<64, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -3,11 +3,28 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "bdattn.h"
+
 namespace bdattn {
+
+// The clean key segment (segment 0) in one buffer (n = 1: k[0], v[0]) or split
+// over n buffers of len rows each, the last holding the rest: row r of the
+// segment is row r - i len of buffer i = min(r / len, n - 1).  len is a multiple
+// of BDATTN_BWD_BN (and so of every key tile and forward step) when n > 1, so a
+// tile never straddles two buffers.
+struct KvShardTable {
+  const void *k[BDATTN_MAX_SHARDS], *v[BDATTN_MAX_SHARDS];
+  int32_t n, len;
+};
+// Gradient buffers of the same split (backward only).
+struct GradShardTable {
+  void *dk[BDATTN_MAX_SHARDS], *dv[BDATTN_MAX_SHARDS];
+};
 
 struct FwdArgs {
   const void *q;            // [n_q][h_q][d] bf16
-  const void *k[2], *v[2];  // per key segment: [n][h_kv][d] bf16
+  const void *k[2], *v[2];  // per key segment: [n][h_kv][d] bf16 (segment 0: sh.k[0], sh.v[0])
+  KvShardTable sh;          // segment 0's buffers
   int32_t n_seg[2];
   void *o;                  // [n_q][h_q][d], fp32 or bf16
   float *lse;               // [h_q][n_q]
@@ -20,11 +37,13 @@ struct FwdArgs {
 
 struct BwdArgs {
   const void *q, *dout;     // [n_q][h_q][d] bf16
-  const void *k[2], *v[2];  // per segment: [n][h_kv][d] bf16
+  const void *k[2], *v[2];  // per segment: [n][h_kv][d] bf16 (segment 0: sh.k[0], sh.v[0])
+  KvShardTable sh;          // segment 0's buffers
+  GradShardTable gsh;       // segment 0's gradient buffers, split as sh
   int32_t n_seg[2];
   const float *lse, *delta; // [h_q][n_q]
   float *dq;                // [n_q][h_q][d] fp32, accumulated
-  void *dk[2], *dv[2];      // per segment: [n][h_kv][d] bf16
+  void *dk[2], *dv[2];      // per segment: [n][h_kv][d] bf16 (segment 0: gsh.dk[0], gsh.dv[0])
   const int32_t *rows;      // [n_q][4]
   const int32_t *items;     // [n_items][12] query tiles of the dQ kernel (the forward tiling)
   const int32_t *bq;        // [n_bq][12] query tiles of the dK/dV kernel

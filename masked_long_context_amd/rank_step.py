@@ -24,7 +24,9 @@ gradients.  When a single shard has legal pairs -- in particular when the whole
 clean K/V is resident and passed as one range -- its forward writes the bf16
 output and the LSE directly: no fp32 partial and no merge.  A whole step can
 also be captured once as a HIP graph and replayed (StepGraph), which removes
-the per-call launch cost of small, launch-bound problems.  This module only
+the per-call launch cost of small, launch-bound problems.  ResidentShardsStep
+runs the same step with every shard resident in its own buffer as one launch
+per kernel over all of them (online merge in registers, no partials).  This module only
 sequences calls and owns buffers; every arithmetic step runs in libbdattn.so.
 """
 from __future__ import annotations
@@ -191,6 +193,127 @@ class BdlmRankStep:
         self.check_inputs(q, k_clean, v_clean, k_corr, v_corr, dout)
         self._forward(q, k_clean, v_clean, k_corr, v_corr)
         return self._backward(q, k_clean, v_clean, k_corr, v_corr, dout)
+
+
+class ResidentShardsStep:
+    """One rank step with every clean shard it attends resident, each in the buffer
+    it arrived in (the fused multi-shard form).  One plan covers the span of the
+    shards, and each kernel runs once over all of them, reading the clean K/V
+    through a table of buffers.  The online softmax then merges the shards in
+    registers: no fp32 partials, no merge call, one launch per kernel however many
+    shards there are:
+
+        bdattn_fwd_shards       -> O (fp32), LSE
+        bdattn_cast_f32_bf16    -> O (bf16, the layer output)
+        bdattn_bwd_prepare      -> delta from the fp32 O, cleared dQ accumulator
+        bdattn_bwd_dkdv_shards  -> dK, dV into one buffer per shard (and the local corrupted ones)
+        bdattn_bwd_dq_shards    -> dQ accumulated
+        bdattn_dq_finalize      -> dQ (bf16)
+
+    shards: (offset, length, local) of consecutive clean ranges, as for
+    BdlmRankStep; every shard but the last holds the same number of positions, a
+    multiple of 128 (the library's shard alignment)."""
+
+    def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda", exact_delta: bool = True):
+        shards = list(shards)
+        if not shards:
+            raise ValueError("no shards")
+        off0, pos = shards[0][0], shards[0][0]
+        for (off, n, _) in shards:
+            if off != pos:
+                raise ValueError("the shards must be consecutive clean ranges")
+            pos += n
+        total = pos - off0
+        self.shard_lens = [n for (_, n, _) in shards]
+        if B.shard_split(total, len(shards), self.shard_lens[0] if len(shards) > 1 else 0) != self.shard_lens:
+            raise ValueError(f"shard lengths {self.shard_lens}: every shard but the last must hold the same "
+                             f"number of positions")
+        self.problem, self.shards, self.device = problem, shards, device
+        self.plan = B.Plan.from_problem(problem.with_kv(off0, total, any(loc for (_, _, loc) in shards)))
+        p = problem
+        self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
+        self.has_corr = self.plan.n_kv(1) > 0
+        self.ws = B.workspace(self.plan.workspace_bytes, device)
+        q_shape = (self.n_q, self.h_q, self.d)
+        self.o = torch.empty(q_shape, dtype=torch.bfloat16, device=device)
+        self.o32 = torch.empty(q_shape, dtype=torch.float32, device=device) if exact_delta else None
+        self.lse = torch.empty((self.h_q, self.n_q), dtype=torch.float32, device=device)
+        self.delta = torch.empty((self.h_q, self.n_q), dtype=torch.float32, device=device)
+        self.dq_acc = torch.empty(q_shape, dtype=torch.float32, device=device)
+        self.dq = torch.empty(q_shape, dtype=torch.bfloat16, device=device)
+        kv = lambda n: torch.empty((n, self.h_kv, self.d), dtype=torch.bfloat16, device=device)
+        self.dk_shards = [kv(n) for n in self.shard_lens]
+        self.dv_shards = [kv(n) for n in self.shard_lens]
+        self.dk_corr = kv(p.n_corr) if self.has_corr else None
+        self.dv_corr = kv(p.n_corr) if self.has_corr else None
+        self.timer = None      # optional callable(tag) -> context manager around each library call
+        self._kv = None        # the bdattn_kv_shards struct of the current call's buffers
+
+    @property
+    def useful_pairs(self) -> int:
+        return self.plan.useful_pairs
+
+    def _t(self, tag):
+        import contextlib
+        return self.timer(tag) if self.timer is not None else contextlib.nullcontext()
+
+    def check_inputs(self, q, k_shards, v_shards, k_corr, v_corr, dout=None):
+        """The caller's tensors against the plan (once per call of forward or
+        backward; the library calls of the step then go unchecked)."""
+        bf = (torch.bfloat16,)
+        if len(k_shards) != len(self.shard_lens) or len(v_shards) != len(self.shard_lens):
+            raise B.BdattnError(B.EINVAL, f"expected {len(self.shard_lens)} K and V shard buffers")
+        named = [(q, "q", (self.n_q, self.h_q, self.d), bf)]
+        for i, n in enumerate(self.shard_lens):
+            named += [(k_shards[i], f"k_shards[{i}]", (n, self.h_kv, self.d), bf),
+                      (v_shards[i], f"v_shards[{i}]", (n, self.h_kv, self.d), bf)]
+        if self.has_corr:
+            cr = (self.problem.n_corr, self.h_kv, self.d)
+            named += [(k_corr, "k_corr", cr, bf), (v_corr, "v_corr", cr, bf)]
+        if dout is not None:
+            named.append((dout, "dout", (self.n_q, self.h_q, self.d), bf))
+        B.check_inputs(named, [("o", self.o.device)])
+        self._kv = B.make_shards(k_shards, v_shards, self.dk_shards, self.dv_shards)
+
+    def forward(self, q, k_shards, v_shards, k_corr, v_corr):
+        self.check_inputs(q, k_shards, v_shards, k_corr, v_corr)
+        return self._forward(q, k_corr, v_corr)
+
+    def _forward(self, q, k_corr, v_corr):
+        st = B.current_stream_handle()
+        kx, vx = (k_corr, v_corr) if self.has_corr else (None, None)
+        out = self.o32 if self.o32 is not None else self.o
+        with self._t("fwd"):
+            B.fwd_shards_unchecked(self.plan, q, self._kv, kx, vx, out, self.lse, self.ws, st)
+        if self.o32 is not None:
+            with self._t("cast"):
+                B.cast_unchecked(self.o32, self.o, st)
+        return self.o, self.lse
+
+    def backward(self, q, k_shards, v_shards, k_corr, v_corr, dout):
+        self.check_inputs(q, k_shards, v_shards, k_corr, v_corr, dout)
+        return self._backward(q, k_corr, v_corr, dout)
+
+    def _backward(self, q, k_corr, v_corr, dout):
+        st = B.current_stream_handle()
+        kx, vx = (k_corr, v_corr) if self.has_corr else (None, None)
+        with self._t("prepare"):
+            B.bwd_prepare_unchecked(self.plan, self.o32 if self.o32 is not None else self.o, dout, self.delta,
+                                    self.dq_acc, st)
+        with self._t("dkdv"):
+            B.bwd_dkdv_shards_unchecked(self.plan, q, self._kv, kx, vx, dout, self.lse, self.delta, self.dk_corr,
+                                        self.dv_corr, self.ws, st)
+        with self._t("dq"):
+            B.bwd_dq_shards_unchecked(self.plan, q, self._kv, kx, vx, dout, self.lse, self.delta, self.dq_acc,
+                                      self.ws, st)
+        with self._t("finalize"):
+            B.dq_finalize_unchecked(self.dq_acc, self.dq, st)
+        return self.dq, self.dk_shards, self.dv_shards, self.dk_corr, self.dv_corr
+
+    def step(self, q, k_shards, v_shards, k_corr, v_corr, dout):
+        self.check_inputs(q, k_shards, v_shards, k_corr, v_corr, dout)
+        self._forward(q, k_corr, v_corr)
+        return self._backward(q, k_corr, v_corr, dout)
 
 
 class StepGraph:

@@ -313,3 +313,127 @@ def test_dkdv_split_choice_and_override():
     assert small.workspace_bytes == unsplit
     small.set_dkdv_split(0)
     assert small.workspace_bytes == base
+
+
+def _shard_plan():
+    # 384 clean keys of the call: three buffers of 128
+    return B.Plan.bdlm(**_problem(clean_len=512, kv_clean_len=384))
+
+
+def _table(n=3, length=128, good=1 << 20, **set_):
+    """A bdattn_kv_shards struct over fake device addresses; set_ maps 'k1' (array k,
+    entry 1) and the like to a replacement address (0 = NULL)."""
+    t = B.KvShards()
+    t.n_shards, t.shard_len = n, length
+    for i in range(B.MAX_SHARDS):
+        t.k[i] = t.v[i] = t.dk[i] = t.dv[i] = good
+    for key, val in set_.items():
+        getattr(t, key[:-1])[int(key[-1])] = val or None
+    return t
+
+
+def test_shard_table_argument_errors_before_any_hip_call():
+    """bdattn_fwd_shards and the bdattn_bwd*_shards calls check the buffer table against
+    the plan's clean range (count, alignment, coverage, pointers) before any HIP call."""
+    lib = B.lib()
+    plan = _shard_plan()
+    assert plan.n_kv(0) == 384
+    good = 1 << 20
+    p_ = _addr(good)
+    ws_n = plan.workspace_bytes
+
+    def fwd(t, ws_bytes=ws_n):
+        kv = None if t is None else ctypes.byref(t)
+        return lib.bdattn_fwd_shards(plan.handle, p_, kv, p_, p_, p_, B.F32, p_, p_, ws_bytes, None)
+
+    assert fwd(None) == B.EINVAL
+    assert fwd(_table(n=0)) == B.EINVAL
+    assert fwd(_table(n=B.MAX_SHARDS + 1)) == B.EINVAL
+    assert fwd(_table(length=100)) == B.EALIGN
+    assert fwd(_table(length=0)) == B.EALIGN
+    assert fwd(_table(length=-128)) == B.EALIGN
+    assert fwd(_table(length=256)) == B.EINVAL          # the third buffer would hold nothing
+    assert fwd(_table(n=2, length=128)) == B.EINVAL      # 256 positions cannot hold 384
+    assert fwd(_table(n=2, length=1 << 40)) == B.EINVAL  # huge lengths do not wrap
+    assert fwd(_table(k1=0)) == B.EINVAL
+    assert fwd(_table(v2=good + 8)) == B.EALIGN
+    # a valid table gets as far as the workspace check (shard_len is ignored for one buffer)
+    assert fwd(_table(), ws_bytes=8) == B.EWORKSPACE
+    assert fwd(_table(n=1, length=7), ws_bytes=8) == B.EWORKSPACE
+    assert fwd(_table(n=2, length=256), ws_bytes=8) == B.EWORKSPACE   # last buffer holds 128
+
+    def bwd(fn, t, n_ptrs, ws_bytes=ws_n):
+        return fn(plan.handle, p_, ctypes.byref(t), *([p_] * n_ptrs), ws_bytes, None)
+
+    # bdattn_bwd_shards: k_corr v_corr dout lse delta dq dk_corr dv_corr ws (9 pointers)
+    assert bwd(lib.bdattn_bwd_shards, _table(dk1=0), 9) == B.EINVAL
+    assert bwd(lib.bdattn_bwd_shards, _table(dv0=good + 4), 9) == B.EALIGN
+    assert bwd(lib.bdattn_bwd_shards, _table(length=96), 9) == B.EALIGN
+    assert bwd(lib.bdattn_bwd_shards, _table(), 9, ws_bytes=8) == B.EWORKSPACE
+    # dK/dV only (8 pointers): gradient buffers needed
+    assert bwd(lib.bdattn_bwd_dkdv_shards, _table(dv2=0), 8) == B.EINVAL
+    assert bwd(lib.bdattn_bwd_dkdv_shards, _table(), 8, ws_bytes=8) == B.EWORKSPACE
+    # dQ only (7 pointers): the gradient entries are not read, so NULL ones pass the table check
+    t = _table()
+    for i in range(B.MAX_SHARDS):
+        t.dk[i] = t.dv[i] = None
+    assert bwd(lib.bdattn_bwd_dq_shards, t, 7, ws_bytes=8) == B.EWORKSPACE
+    assert bwd(lib.bdattn_bwd_dq_shards, _table(k0=0), 7) == B.EINVAL
+    assert lib.bdattn_fwd_shards(None, p_, ctypes.byref(_table()), p_, p_, p_, B.F32, p_, p_, ws_n, None) == B.EINVAL
+
+
+def test_shard_split_rules():
+    assert B.shard_split(384, 3, 128) == [128, 128, 128]
+    assert B.shard_split(300, 3, 128) == [128, 128, 44]
+    assert B.shard_split(77, 1, 0) == [77]
+    assert _status(lambda: B.shard_split(256, 3, 128)) == B.EINVAL
+    assert _status(lambda: B.shard_split(384, 2, 128)) == B.EINVAL
+    assert _status(lambda: B.shard_split(384, 3, 100)) == B.EALIGN
+    assert _status(lambda: B.shard_split(384, 0, 128)) == B.EINVAL
+    assert _status(lambda: B.shard_split(384, B.MAX_SHARDS + 1, 128)) == B.EINVAL
+
+
+def test_binding_checks_shard_buffers():
+    """bdattn_fwd_shards in the binding: each buffer's dtype, length (from the split),
+    contiguity, then the device (CPU tensors reach only the last check)."""
+    import torch
+    plan = _shard_plan()
+    n_q, hq, d = plan.q_shape()
+    _, hkv, _ = plan.kv_shape(0)
+    kv1 = plan.kv_shape(1)
+    f32 = torch.float32
+    ks = [_cpu((128, hkv, d)) for _ in range(3)]
+    vs = [_cpu((128, hkv, d)) for _ in range(3)]
+    ok = dict(q=_cpu((n_q, hq, d)), k_shards=ks, v_shards=vs, k_corr=_cpu(kv1), v_corr=_cpu(kv1),
+              o=_cpu((n_q, hq, d), f32), lse=_cpu((hq, n_q), f32), ws=_cpu((plan.workspace_bytes,), torch.uint8))
+    call = lambda **kw: B.bdattn_fwd_shards(plan, **{**ok, **kw})
+
+    def err(code, text, **kw):
+        with pytest.raises(B.BdattnError) as e:
+            call(**kw)
+        assert e.value.status == code and text in str(e.value), str(e.value)
+
+    err(B.EINVAL, "must be a GPU tensor")
+    err(B.EINVAL, "same length", v_shards=vs[:2])
+    err(B.EINVAL, "k_shards[2] has shape", k_shards=ks[:2] + [_cpu((64, hkv, d))])
+    err(B.EUNSUPPORTED, "v_shards[1] has dtype", v_shards=[vs[0], _cpu((128, hkv, d), f32), vs[2]])
+    err(B.EINVAL, "v_shards[0] must be contiguous",
+        v_shards=[_cpu((hkv, 128, d)).transpose(0, 1), vs[1], vs[2]])
+    err(B.EALIGN, "multiple of 128", k_shards=[_cpu((96, hkv, d))] * 4, v_shards=[_cpu((96, hkv, d))] * 4)
+    # the backward's gradient lists are checked the same way
+    with pytest.raises(B.BdattnError) as e:
+        B.bdattn_bwd_dkdv_shards(plan, ok["q"], ks, vs, ok["k_corr"], ok["v_corr"], _cpu((n_q, hq, d)),
+                                 ok["lse"], _cpu((hq, n_q), f32), ks, vs[:1], _cpu(kv1), _cpu(kv1), ok["ws"])
+    assert e.value.status == B.EINVAL and "one tensor per K/V buffer" in str(e.value)
+
+
+def test_resident_shards_step_rejects_uneven_or_gapped_shards():
+    from masked_long_context_amd import workloads as wl
+    from masked_long_context_amd.rank_step import ResidentShardsStep
+    cfg = wl.small_bdlm_config(512, 16, 4, 1, 4, 2, 128, 4)
+    with pytest.raises(ValueError, match="consecutive"):
+        ResidentShardsStep(cfg.problem, [(0, 128, False), (256, 128, True)])
+    with pytest.raises(B.BdattnError):
+        ResidentShardsStep(cfg.problem, [(0, 256, False), (256, 128, False), (384, 128, True)])
+    with pytest.raises(B.BdattnError):
+        ResidentShardsStep(cfg.problem, [(0, 96, False), (96, 96, False), (192, 320, True)])
