@@ -273,6 +273,57 @@ void rejections() {
   bdattn_plan_destroy(nullptr);
 }
 
+// Random buffer tables of the *_shards entry points against a brute-force
+// reading of their rules: a valid table must get as far as the workspace check
+// (the workspace is one byte short), so no call reaches a launch.
+void fuzz_shards(int iters) {
+  std::vector<int64_t> owned = {20, 3};
+  bdattn_problem pr{};
+  pr.clean_len = 1024; pr.block_size = 32; pr.q_clean_offset = 128; pr.q_clean_len = 256;
+  pr.owned_blocks = owned.data(); pr.n_owned = 2; pr.kv_clean_offset = 128; pr.kv_clean_len = 640;
+  pr.with_local_corrupt = 1; pr.h_q = 4; pr.h_kv = 2; pr.head_dim = 64;
+  bdattn_plan *p = nullptr;
+  EXPECT(bdattn_plan_create(&pr, &p) == BDATTN_OK, "shard problem");
+  if (!p) return;
+  const int64_t n0 = bdattn_plan_n_kv(p, 0), ws = bdattn_plan_workspace_bytes(p);
+  EXPECT(n0 == 640, "shard problem keys");
+  void *g = reinterpret_cast<void *>(uintptr_t(1) << 20);
+  float *gf = static_cast<float *>(g);
+  const int64_t lens[] = {0, -128, 64, 100, 128, 192, 256, 320, 384, 640, 768, int64_t(1) << 40, 130};
+  for (int it = 0; it < iters; ++it) {
+    bdattn_kv_shards t{};
+    t.n_shards = (int32_t)rnd_in(-2, 20);
+    t.shard_len = lens[rnd_in(0, (int64_t)(sizeof(lens) / sizeof(lens[0])) - 1)];
+    for (int i = 0; i < BDATTN_MAX_SHARDS; ++i) t.k[i] = t.v[i] = t.dk[i] = t.dv[i] = g;
+    const bool grads = rnd_in(0, 1) == 1;
+    // at most one bad entry: field f of entry e, NULL or misaligned
+    const int f = (int)rnd_in(0, 4), e = (int)rnd_in(0, BDATTN_MAX_SHARDS - 1);
+    const bool null_ptr = rnd_in(0, 1) == 1;
+    void *bad = null_ptr ? nullptr : reinterpret_cast<void *>((uintptr_t(1) << 20) + 4);
+    if (f == 0) t.k[e] = bad;
+    if (f == 1) t.v[e] = bad;
+    if (f == 2) t.dk[e] = bad;
+    if (f == 3) t.dv[e] = bad;
+    int want = BDATTN_EWORKSPACE;
+    const int n = t.n_shards;
+    if (n < 1 || n > BDATTN_MAX_SHARDS) {
+      want = BDATTN_EINVAL;
+    } else if (n > 1 && (t.shard_len <= 0 || t.shard_len % BDATTN_SHARD_ALIGN != 0)) {
+      want = BDATTN_EALIGN;
+    } else if (n > 1 && !(t.shard_len < n0 && (n - 1) * t.shard_len < n0 && n0 <= n * t.shard_len)) {
+      want = BDATTN_EINVAL;
+    } else if (f < 4 && e < n && (f < 2 || grads)) {
+      want = null_ptr ? BDATTN_EINVAL : BDATTN_EALIGN;
+    }
+    const int rc = grads ? bdattn_bwd_dkdv_shards(p, g, &t, g, g, g, gf, gf, g, g, g, ws - 1, nullptr)
+                         : bdattn_fwd_shards(p, g, &t, g, g, g, BDATTN_F32, gf, g, ws - 1, nullptr);
+    EXPECT(rc == want, "shard table n=%d len=%lld field %d entry %d %s: got %d, want %d", n,
+           (long long)t.shard_len, f, e, null_ptr ? "NULL" : "misaligned", rc, want);
+  }
+  EXPECT(bdattn_fwd_shards(p, g, nullptr, g, g, g, BDATTN_F32, gf, g, ws, nullptr) == BDATTN_EINVAL, "kv NULL");
+  bdattn_plan_destroy(p);
+}
+
 }  // namespace
 
 int main(int argc, char **argv) {
@@ -280,10 +331,12 @@ int main(int argc, char **argv) {
   fuzz_bdlm(iters);
   fuzz_varlen_and_tasks(iters);
   rejections();
+  fuzz_shards(iters * 10);
   if (g_fail) {
     std::printf("%d checks failed\n", g_fail);
     return 1;
   }
-  std::printf("ok: %d random BDLM plans, %d varlen/task/splitter cases, every rejection path\n", iters, iters);
+  std::printf("ok: %d random BDLM plans, %d varlen/task/splitter cases, %d shard tables, every rejection path\n",
+              iters, iters, iters * 10);
   return 0;
 }
