@@ -381,7 +381,7 @@ def bench_varlen(args, cfg):
                    "flops_per_step": flops, **extra},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "plan_ms": round(plan_ms, 2),
-        "roofline": {"kernel": f"dkdv_kernel<{d}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
+        "roofline": {"kernel": f"dkdv_kernel<{d}, false>", "bound": "mfma", "achieved": round(dk_achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(cfg.name), "algorithmic_bytes": dk_alg_bytes,
                      "ms_per_launch": round(dkdv_ms, 4), "flops_per_launch": dk_flops},
@@ -584,7 +584,8 @@ def main():
                    "flops_per_step": flops},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "plan_ms": round(plan_ms, 2),
-        "roofline": {"kernel": f"dkdv_kernel<{p.head_dim}>", "bound": "mfma", "achieved": round(dk_achieved, 2),
+        "roofline": {"kernel": f"dkdv_kernel<{p.head_dim}, {'true' if args.fused and n_sh > 1 else 'false'}>",
+                     "bound": "mfma", "achieved": round(dk_achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dk_achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(workload), "algorithmic_bytes": dk_alg_bytes,
                      "ms_per_launch": round(dk["ms_per_launch"], 4),

@@ -33,7 +33,7 @@ import fullsize_ref as fr
 import oracle
 from masked_long_context_amd import workloads as wl
 from masked_long_context_amd import bdattn as B
-from masked_long_context_amd.rank_step import BdlmRankStep, TaskStep, VarlenStep
+from masked_long_context_amd.rank_step import BdlmRankStep, ResidentShardsStep, TaskStep, VarlenStep
 from gpu_util import TOL_REL_L2, check_close, check_lse, need_gpu, poison_
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
@@ -126,18 +126,45 @@ def run_bdlm_fullsize(idx, n_rows, fused=False, every_element=False):
     log(f"{cfg.name}: generating inputs")
     inp = wl.bdlm_inputs(cfg, seed=0)
     g = {k: v.cuda() for k, v in inp.items()}
-    shards = [(0, p.clean_len, True)] if fused else cfg.shards
-    step = BdlmRankStep(p, shards)
-    assert step.direct == fused
-    poison_(step.o_parts, step.lse_parts, step.o, step.o32, step.lse, step.dq, step.dk_clean, step.dv_clean,
-            step.dk_corr, step.dv_corr)
-    log(f"{cfg.name}: GPU step ({len(shards)} clean K/V range(s))")
-    step.step(g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
-    torch.cuda.synchronize()
-    o, lse, dq = step.o.cpu(), step.lse.cpu(), step.dq.cpu()
-    dk = torch.cat([step.dk_clean, step.dk_corr]).cpu()
-    dv = torch.cat([step.dv_clean, step.dv_corr]).cpu()
-    del g, step
+    if fused:
+        # every clean shard resident in a buffer of its own, one launch per kernel
+        step = ResidentShardsStep(p, cfg.shards)
+        k_sh = [g["k_clean"][o_:o_ + n_].clone() for (o_, n_, _) in cfg.shards]
+        v_sh = [g["v_clean"][o_:o_ + n_].clone() for (o_, n_, _) in cfg.shards]
+        poison_(step.o, step.o32, step.lse, step.dq, *step.dk_shards, *step.dv_shards, step.dk_corr, step.dv_corr)
+        log(f"{cfg.name}: GPU step ({len(k_sh)} resident shard buffers, one launch per kernel)")
+        step.step(g["q"], k_sh, v_sh, g["k_corr"], g["v_corr"], g["dout"])
+        torch.cuda.synchronize()
+        o, lse, dq = step.o.cpu(), step.lse.cpu(), step.dq.cpu()
+        dk = torch.cat(step.dk_shards + [step.dk_corr]).cpu()
+        dv = torch.cat(step.dv_shards + [step.dv_corr]).cpu()
+        del step, k_sh, v_sh
+        # the same plan with the clean K/V in one buffer: the same bits
+        one = BdlmRankStep(p, [(0, p.clean_len, True)])
+        assert one.direct
+        poison_(one.o, one.o32, one.lse, one.dq, one.dk_clean, one.dv_clean, one.dk_corr, one.dv_corr)
+        log(f"{cfg.name}: GPU step (one buffer, the same plan)")
+        one.step(g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+        torch.cuda.synchronize()
+        for name, a_, b_ in (("o", o, one.o), ("lse", lse, one.lse), ("dq", dq, one.dq),
+                             ("dk", dk, torch.cat([one.dk_clean, one.dk_corr])),
+                             ("dv", dv, torch.cat([one.dv_clean, one.dv_corr]))):
+            assert torch.equal(a_, b_.cpu()), f"resident shards vs one buffer: {name} differs"
+        log(f"{cfg.name}: resident shards and one buffer agree bit for bit")
+        del one
+    else:
+        step = BdlmRankStep(p, cfg.shards)
+        assert not step.direct
+        poison_(step.o_parts, step.lse_parts, step.o, step.o32, step.lse, step.dq, step.dk_clean, step.dv_clean,
+                step.dk_corr, step.dv_corr)
+        log(f"{cfg.name}: GPU step ({len(cfg.shards)} clean K/V ranges)")
+        step.step(g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+        torch.cuda.synchronize()
+        o, lse, dq = step.o.cpu(), step.lse.cpu(), step.dq.cpu()
+        dk = torch.cat([step.dk_clean, step.dk_corr]).cpu()
+        dv = torch.cat([step.dv_clean, step.dv_corr]).cpu()
+        del step
+    del g
     for t in (o, lse, dq, dk, dv):
         assert not torch.isnan(t.float()).any(), "unwritten output"
     G = p.h_q // p.h_kv
@@ -171,7 +198,9 @@ def test_csbp_256k_rank_share_fullsize():
 
 
 def test_csbp_256k_rank_share_fused_fullsize():
-    """All sixteen clean shards resident and passed as one range (no partials, no merge)."""
+    """All sixteen clean shards resident, each in a buffer of its own, and one launch per
+    kernel over all of them (no partials, no merge); bit for bit the same plan run with
+    the clean K/V in one buffer."""
     run_bdlm_fullsize(3, n_rows=1024, fused=True)
 
 
