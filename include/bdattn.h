@@ -158,6 +158,20 @@ void bdattn_plan_destroy(bdattn_plan *plan);
  * and, when the plan splits its dK/dV key tiles, the fp32 dK/dV partials. */
 int64_t bdattn_plan_workspace_bytes(const bdattn_plan *plan);
 
+/* Keeps the plan's tables in `workspace` (>= bdattn_plan_workspace_bytes, 256-byte
+ * aligned): copies them there once, on `stream`, and every later compute call
+ * given this plan and this same workspace skips its own upload (a host-to-device
+ * copy that the call's kernels would wait for).  For a plan run many times, such
+ * as one rank's shard in every training step.  Calls with another workspace
+ * upload as before.  A plan keeps at most one workspace (a new call replaces the
+ * previous one), and a workspace holds one plan's tables: an upload of another
+ * plan's tables into it (any call, or this one) ends the first plan's claim.
+ * workspace NULL: ends this plan's claim.  The library cannot see other writes:
+ * while the tables are kept the caller must not write the workspace (other than
+ * through this plan's calls) nor free it; end the claim first (or destroy the
+ * plan).  Errors: EINVAL (plan NULL), EALIGN, EWORKSPACE, EHIP. */
+int bdattn_plan_keep_tables(bdattn_plan *plan, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Workgroups per key tile of the dK/dV kernel (a schedule choice; results do not
  * depend on it beyond fp32 rounding order, and are deterministic for each value).
  * With one, each workgroup walks every query tile that attends its 128 keys and

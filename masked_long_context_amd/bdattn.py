@@ -66,6 +66,7 @@ _SIGS = {
                                    ctypes.POINTER(c_int32), ctypes.POINTER(c_int32), c_int64]),
     "bdattn_plan_destroy": (None, [c_void_p]),
     "bdattn_plan_workspace_bytes": (c_int64, [c_void_p]),
+    "bdattn_plan_keep_tables": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p]),
     "bdattn_plan_useful_pairs": (c_int64, [c_void_p]),
     "bdattn_plan_set_dkdv_split": (c_int32, [c_void_p, c_int32]),
     "bdattn_plan_dkdv_split": (c_int32, [c_void_p]),
@@ -263,6 +264,20 @@ class Plan:
     def set_dkdv_split(self, split: int):
         """0 = automatic, 1..8 = dK/dV workgroups per key tile (before first use)."""
         _check(lib().bdattn_plan_set_dkdv_split(self._h, split))
+
+    def keep_tables(self, ws, stream=None):
+        """Upload the plan's tables into `ws` once; later calls with this plan and this
+        workspace skip their per-call upload (bdattn_plan_keep_tables).  The workspace
+        must stay untouched, and alive, while kept: ws None ends the claim."""
+        if ws is None:
+            _check(lib().bdattn_plan_keep_tables(self._h, None, 0, None))
+            self._kept = None
+            return
+        dev = []
+        _want_ws(ws, self, dev)
+        _on_one_gpu(dev, stream)
+        _check(lib().bdattn_plan_keep_tables(self._h, _ptr(ws), ws.numel(), _stream(stream)))
+        self._kept = ws   # holds the buffer alive while the tables are kept in it
 
     @property
     def n_q(self) -> int:

@@ -9,6 +9,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
 
 #include "kernels/kernels.h"
 #include "plan.h"
@@ -130,9 +131,26 @@ void fill_shards(const bdattn_kv_shards &kv, bdattn::KvShardTable &t, bdattn::Gr
   }
 }
 
-// Copies the plan's tables into the head of `dst` on `stream`.
-int upload(bdattn_plan *pl, void *dst, hipStream_t stream) {
+// Workspaces that hold a kept plan's tables, and the plan; an upload of another
+// plan's tables into one of them ends that plan's claim.
+std::mutex g_kept_mu;
+std::unordered_map<const void *, bdattn_plan *> g_kept;
+
+// Copies the plan's tables into the head of `dst` on `stream`, unless `dst` holds
+// them already (kept by this plan) and `force` is false.
+int upload(bdattn_plan *pl, void *dst, hipStream_t stream, bool force = false) {
   bdattn::Plan &p = pl->p;
+  {
+    std::lock_guard<std::mutex> kl(g_kept_mu);
+    auto it = g_kept.find(dst);
+    if (it != g_kept.end()) {
+      if (it->second == pl && !force) return BDATTN_OK;
+      if (it->second != pl) {   // another plan's tables are about to be overwritten
+        it->second->tables_at = nullptr;
+        g_kept.erase(it);
+      }
+    }
+  }
   {
     std::lock_guard<std::mutex> lk(pl->mu);
     if (!p.pinned) {
@@ -145,6 +163,16 @@ int upload(bdattn_plan *pl, void *dst, hipStream_t stream) {
   }
   HIP_CHECK(hipMemcpyAsync(dst, p.pinned, p.image.size(), hipMemcpyHostToDevice, stream), "hipMemcpyAsync");
   return BDATTN_OK;
+}
+
+// Ends the plan's claim on its kept workspace, if any.
+void release_kept(bdattn_plan *pl) {
+  std::lock_guard<std::mutex> kl(g_kept_mu);
+  if (pl->tables_at) {
+    auto it = g_kept.find(pl->tables_at);
+    if (it != g_kept.end() && it->second == pl) g_kept.erase(it);
+    pl->tables_at = nullptr;
+  }
 }
 
 const int32_t *img(const void *base, int64_t off) {
@@ -394,6 +422,7 @@ int bdattn_plan_create_varlen(const int32_t *cu, int32_t n_seqs, int32_t causal,
 
 void bdattn_plan_destroy(bdattn_plan *pl) {
   if (!pl) return;
+  release_kept(pl);
   if (pl->p.pinned) {
     if (pl->p.used) (void)hipDeviceSynchronize();   // uploads may still read the pinned copy
     (void)hipHostFree(pl->p.pinned);
@@ -402,6 +431,23 @@ void bdattn_plan_destroy(bdattn_plan *pl) {
 }
 
 int64_t bdattn_plan_workspace_bytes(const bdattn_plan *pl) { return pl ? pl->p.ws_bytes : BDATTN_EINVAL; }
+
+int bdattn_plan_keep_tables(bdattn_plan *pl, void *ws, int64_t ws_bytes, void *stream) {
+  if (!pl) return fail(BDATTN_EINVAL, "plan is NULL");
+  if (!ws) {
+    release_kept(pl);
+    return BDATTN_OK;
+  }
+  int rc = check_ws(pl->p, ws, ws_bytes);
+  if (rc != BDATTN_OK) return rc;
+  release_kept(pl);   // one kept workspace per plan
+  rc = upload(pl, ws, (hipStream_t)stream, true);
+  if (rc != BDATTN_OK) return rc;
+  std::lock_guard<std::mutex> kl(g_kept_mu);
+  g_kept[ws] = pl;
+  pl->tables_at = ws;
+  return BDATTN_OK;
+}
 int64_t bdattn_plan_useful_pairs(const bdattn_plan *pl) { return pl ? pl->p.useful_pairs : BDATTN_EINVAL; }
 int64_t bdattn_plan_n_q(const bdattn_plan *pl) { return pl ? pl->p.n_q : BDATTN_EINVAL; }
 int bdattn_plan_set_dkdv_split(bdattn_plan *pl, int32_t split) {

@@ -11,6 +11,10 @@
 struct bdattn_plan {
   bdattn::Plan p;
   std::mutex mu;   // guards the lazily made pinned copy of the tables and `used`
+  // Workspace that holds this plan's tables (bdattn_plan_keep_tables), whose
+  // calls then skip the upload; NULL when none.  Guarded by the library-wide
+  // registry of kept workspaces, not by `mu`.
+  const void *tables_at = nullptr;
 };
 
 namespace bdattn {

@@ -38,9 +38,21 @@ import torch
 from . import bdattn as B
 
 
+def keep_workspaces(plans, device):
+    """One workspace per plan, holding that plan's tables (bdattn_plan_keep_tables):
+    uploaded once here, on the current stream, which is then synchronized so that
+    the step may run on any stream."""
+    wss = [B.workspace(pl.workspace_bytes, device) for pl in plans]
+    for pl, ws in zip(plans, wss):
+        pl.keep_tables(ws)
+    torch.cuda.current_stream(device).synchronize()
+    return wss
+
+
 class BdlmRankStep:
     def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda",
-                 part_dtype=torch.float32, dkdv_split: int = 0, streams: int = 1, exact_delta: bool = True):
+                 part_dtype=torch.float32, dkdv_split: int = 0, streams: int = 1, exact_delta: bool = True,
+                 keep_tables: bool = True):
         self.problem = problem
         self.shards = list(shards)
         self.device = device
@@ -59,6 +71,9 @@ class BdlmRankStep:
         # accumulator, stay on the caller's stream in shard order
         self.side = [torch.cuda.Stream(device=device) for _ in range(max(1, int(streams)) - 1)]
         self.ws_side = [B.workspace(ws_bytes, device) for _ in self.side]
+        # keep_tables: every plan keeps its tables in a workspace of its own, uploaded
+        # once here, so no call of a step waits for a table upload
+        self.ws_plan = keep_workspaces(self.plans, device) if keep_tables else None
         # one active shard: its forward writes O and LSE itself (no partials)
         self.direct = len(self.active) == 1
         n_parts = 0 if self.direct else max(1, len(self.active))
@@ -88,14 +103,15 @@ class BdlmRankStep:
         import contextlib
         return self.timer(tag) if self.timer is not None else contextlib.nullcontext()
 
-    def _lane(self, j):
-        """Stream context and workspace of the j-th independent call (lane 0: the
-        caller's stream)."""
+    def _lane(self, j, i):
+        """Stream context, workspace and stream handle of the j-th independent call,
+        of plan i (lane 0: the caller's stream)."""
         import contextlib
         k = j % (len(self.side) + 1)
+        ws = self.ws_plan[i] if self.ws_plan is not None else (self.ws if k == 0 else self.ws_side[k - 1])
         if k == 0:
-            return contextlib.nullcontext(), self.ws, self._main
-        return torch.cuda.stream(self.side[k - 1]), self.ws_side[k - 1], self.side[k - 1].cuda_stream
+            return contextlib.nullcontext(), ws, self._main
+        return torch.cuda.stream(self.side[k - 1]), ws, self.side[k - 1].cuda_stream
 
     def _fork(self):
         main = torch.cuda.current_stream()
@@ -143,14 +159,14 @@ class BdlmRankStep:
             off, n, local = self.shards[i]
             with self._t("fwd"):
                 B.fwd_unchecked(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
-                                k_corr if local else None, v_corr if local else None, out, self.lse, self.ws,
-                                self._main)
+                                k_corr if local else None, v_corr if local else None, out, self.lse,
+                                self.ws_plan[i] if self.ws_plan is not None else self.ws, self._main)
             self._to_bf16()
             return self.o, self.lse
         self._fork()
         for slot, i in enumerate(self.active):
             off, n, local = self.shards[i]
-            lane, ws, st = self._lane(slot)
+            lane, ws, st = self._lane(slot, i)
             with lane, self._t("fwd"):
                 B.fwd_unchecked(self.plans[i], q, k_clean[off:off + n], v_clean[off:off + n],
                                 k_corr if local else None, v_corr if local else None,
@@ -176,14 +192,14 @@ class BdlmRankStep:
         for i, (off, n, local) in enumerate(self.shards):
             kc, vc = k_clean[off:off + n], v_clean[off:off + n]
             kx, vx = (k_corr, v_corr) if local else (None, None)
-            lane, ws, st = self._lane(i)
+            lane, ws, st = self._lane(i, i)
             with lane, self._t("dkdv"):
                 B.bwd_dkdv_unchecked(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta,
                                      self.dk_clean[off:off + n], self.dv_clean[off:off + n],
                                      self.dk_corr if local else None, self.dv_corr if local else None, ws, st)
             with self._t("dq"):
                 B.bwd_dq_unchecked(self.plans[i], q, kc, vc, kx, vx, dout, self.lse, self.delta, self.dq_acc,
-                                   self.ws, self._main)
+                                   self.ws_plan[i] if self.ws_plan is not None else self.ws, self._main)
         self._join()
         with self._t("finalize"):
             B.dq_finalize_unchecked(self.dq_acc, self.dq, self._main)
@@ -214,7 +230,8 @@ class ResidentShardsStep:
     BdlmRankStep; every shard but the last holds the same number of positions, a
     multiple of 128 (the library's shard alignment)."""
 
-    def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda", exact_delta: bool = True):
+    def __init__(self, problem, shards: Sequence[Tuple[int, int, bool]], device="cuda", exact_delta: bool = True,
+                 keep_tables: bool = True, dkdv_split: int = 0):
         shards = list(shards)
         if not shards:
             raise ValueError("no shards")
@@ -230,10 +247,13 @@ class ResidentShardsStep:
                              f"number of positions")
         self.problem, self.shards, self.device = problem, shards, device
         self.plan = B.Plan.from_problem(problem.with_kv(off0, total, any(loc for (_, _, loc) in shards)))
+        if dkdv_split:   # 0 keeps the plan's automatic choice
+            self.plan.set_dkdv_split(dkdv_split)
         p = problem
         self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
         self.has_corr = self.plan.n_kv(1) > 0
-        self.ws = B.workspace(self.plan.workspace_bytes, device)
+        self.ws = keep_workspaces([self.plan], device)[0] if keep_tables else \
+            B.workspace(self.plan.workspace_bytes, device)
         q_shape = (self.n_q, self.h_q, self.d)
         self.o = torch.empty(q_shape, dtype=torch.bfloat16, device=device)
         self.o32 = torch.empty(q_shape, dtype=torch.float32, device=device) if exact_delta else None
@@ -347,12 +367,13 @@ class VarlenStep:
     """Forward + backward of packed independent shards (one call each)."""
 
     def __init__(self, cu_seqlens, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0, plan=None,
-                 exact_delta: bool = True):
+                 exact_delta: bool = True, keep_tables: bool = True):
         self.plan = plan if plan is not None else B.Plan.varlen(cu_seqlens, causal, h_q, h_kv, head_dim,
                                                                 softmax_scale)
         T, n_keys = self.plan.n_q, self.plan.n_kv(0)
         self.T, self.n_keys, self.h_q, self.h_kv, self.d = T, n_keys, h_q, h_kv, head_dim
-        self.ws = B.workspace(self.plan.workspace_bytes, device)
+        self.ws = keep_workspaces([self.plan], device)[0] if keep_tables else \
+            B.workspace(self.plan.workspace_bytes, device)
         self.o = torch.empty((T, h_q, head_dim), dtype=torch.bfloat16, device=device)
         # fp32 output kept for the backward's delta (see BdlmRankStep)
         self.o32 = torch.empty((T, h_q, head_dim), dtype=torch.float32, device=device) if exact_delta else None
@@ -425,7 +446,7 @@ class TaskStep(VarlenStep):
     [k_cu[-1], h_kv, d]); dk/dv hold one gradient per context row."""
 
     def __init__(self, q_cu, k_cu, causal, h_q, h_kv, head_dim, device="cuda", softmax_scale=0.0,
-                 exact_delta: bool = True):
+                 exact_delta: bool = True, keep_tables: bool = True):
         plan = B.Plan.tasks(q_cu, k_cu, causal, h_q, h_kv, head_dim, softmax_scale)
         super().__init__(None, causal, h_q, h_kv, head_dim, device, softmax_scale, plan=plan,
-                         exact_delta=exact_delta)
+                         exact_delta=exact_delta, keep_tables=keep_tables)

@@ -437,3 +437,19 @@ def test_resident_shards_step_rejects_uneven_or_gapped_shards():
         ResidentShardsStep(cfg.problem, [(0, 256, False), (256, 128, False), (384, 128, True)])
     with pytest.raises(B.BdattnError):
         ResidentShardsStep(cfg.problem, [(0, 96, False), (96, 96, False), (192, 320, True)])
+
+
+def test_keep_tables_argument_errors_before_any_hip_call():
+    lib = B.lib()
+    plan = B.Plan.bdlm(**_problem())
+    good = 1 << 20
+    n = plan.workspace_bytes
+    assert lib.bdattn_plan_keep_tables(None, _addr(good), n, None) == B.EINVAL
+    assert lib.bdattn_plan_keep_tables(plan.handle, _addr(good + 16), n, None) == B.EALIGN
+    assert lib.bdattn_plan_keep_tables(plan.handle, _addr(good), n - 1, None) == B.EWORKSPACE
+    # NULL ends a claim (none held here): no HIP call
+    assert lib.bdattn_plan_keep_tables(plan.handle, None, 0, None) == B.OK
+    plan.keep_tables(None)
+    with pytest.raises(B.BdattnError) as e:
+        plan.keep_tables(_cpu((n,), __import__("torch").uint8))
+    assert e.value.status == B.EINVAL and "GPU tensor" in str(e.value)

@@ -22,9 +22,7 @@ def _gpu():
 
 def run_resident(cfg, inp, shards, split=0):
     g = {k: v.to("cuda") for k, v in inp.items()}
-    step = ResidentShardsStep(cfg.problem, shards)
-    if split:
-        step.plan.set_dkdv_split(split)
+    step = ResidentShardsStep(cfg.problem, shards, dkdv_split=split)
     # one separately allocated buffer per shard, as a rank would receive them
     k_sh = [g["k_clean"][o:o + n].clone() for (o, n, _) in shards]
     v_sh = [g["v_clean"][o:o + n].clone() for (o, n, _) in shards]
