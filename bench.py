@@ -62,6 +62,37 @@ def profiled_traffic(workload: str):
     return int(kv["traffic_bytes_per_launch"])
 
 
+def timed_steps(run_step, steps: int):
+    """Run `steps` steps between two events on the current stream, with an event after
+    each step: the mean step time over the whole span, and the median of the steps."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        run_step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[steps]) / steps, per[len(per) // 2]
+
+
+def aux_bandwidth(tot, steps: int, rows: int, h: int, d: int) -> dict:
+    """Achieved HBM rate of the step's bandwidth-bound calls, from their algorithmic
+    bytes per (row, q-head): preprocess reads the fp32 O (4d) and dO (2d), writes
+    delta (4) and clears the fp32 dQ accumulator (4d); the output cast and the dQ
+    finalize each read 4d and write 2d."""
+    out = {}
+    for tag, per_rowhead in (("prepare", 10 * d + 4), ("cast", 6 * d), ("finalize", 6 * d)):
+        t_ms = tot.get(tag, (0.0, 1))[0] / steps
+        out[f"{tag}_ms"] = round(t_ms, 4)
+        if t_ms > 0:
+            gbs = rows * h * per_rowhead / (t_ms * 1e-3) / 1e9
+            out[f"{tag}_gbs"] = round(gbs, 1)
+            out[f"{tag}_frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+    return out
+
+
 class EventTimer:
     """HIP events on the current stream (the stream the library launches on) around each call."""
 
@@ -337,13 +368,7 @@ def bench_varlen(args, cfg):
         step.step(*a)
     torch.cuda.synchronize()
     timer.enabled = True
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step.step(*a)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, ms_median = timed_steps(lambda: step.step(*a), args.steps)
     tot = timer.totals_ms()
     tflops = flops / (ms * 1e-3) / 1e12
     graph = None
@@ -353,14 +378,8 @@ def bench_varlen(args, cfg):
         for _ in range(args.warmup):
             sg.replay()
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            sg.replay()
-        g1.record()
-        torch.cuda.synchronize()
         graph = {"eager_value": round(tflops, 2), "eager_ms_per_step": round(ms, 4)}
-        ms = g0.elapsed_time(g1) / args.steps
+        ms, ms_median = timed_steps(sg.replay, args.steps)
         tflops = flops / (ms * 1e-3) / 1e12
         del sg
     fwd_ms = tot["fwd"][0] / args.steps
@@ -389,9 +408,10 @@ def bench_varlen(args, cfg):
         "kernels": {"fwd": {"ms": round(fwd_ms, 4), "tflops": round(pairs * cfg.h_q * 4 * d / (fwd_ms * 1e-3) / 1e12, 2)},
                     "dkdv": {"ms": round(dkdv_ms, 4), "tflops": round(dk_achieved, 2)},
                     "dq": {"ms": round(dq_ms, 4), "tflops": round(pairs * cfg.h_q * 6 * d / (dq_ms * 1e-3) / 1e12, 2)},
-                    "cast_ms": round(tot.get("cast", (0.0, 1))[0] / args.steps, 4),
-                    "prepare_ms": round(tot["prepare"][0] / args.steps, 4),
-                    "finalize_ms": round(tot["finalize"][0] / args.steps, 4)},
+                    **aux_bandwidth(tot, args.steps, step.T, cfg.h_q, d)},
+        # the same work counted without the backward's recompute of S (12d per pair)
+        "value_12d": round(pairs * cfg.h_q * 12 * d / (ms * 1e-3) / 1e12, 2),
+        "ms_per_step_median": round(ms_median, 3),
     }
     if graph is not None:
         out["metric"] += " (step replayed from a HIP graph)"
@@ -502,16 +522,10 @@ def main():
         step.step(*args_)
     torch.cuda.synchronize()
     timer.enabled = True
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step.step(*args_)
-    end.record()
-    torch.cuda.synchronize()
+    ms, ms_median = timed_steps(lambda: step.step(*args_), args.steps)
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
     tot = timer.totals_ms()
     tflops = flops / (ms * 1e-3) / 1e12
 
@@ -551,15 +565,9 @@ def main():
         for _ in range(args.warmup):
             sg.replay()
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            sg.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        gms = g0.elapsed_time(g1) / args.steps
         graph = {"eager_value": round(tflops, 2), "eager_ms_per_step": round(ms, 4)}
-        ms, tflops = gms, flops / (gms * 1e-3) / 1e12
+        ms, ms_median = timed_steps(sg.replay, args.steps)
+        tflops = flops / (ms * 1e-3) / 1e12
         del sg
 
     ceiling = None
@@ -598,10 +606,11 @@ def main():
             "merge": {"ms": round(merge_ms / max(merge_n, 1), 4), "parts": n_act, "gbs": round(merge_gbs, 1),
                       "frac_hbm": round(merge_gbs / PEAK_HBM_GBS, 4)},
             "merge_micro": merge_micro,
-            "cast_ms": round(tot.get("cast", (0.0, 1))[0] / args.steps, 4),
-            "prepare_ms": round(tot.get("prepare", (0.0, 1))[0] / args.steps, 4),
-            "finalize_ms": round(tot.get("finalize", (0.0, 1))[0] / args.steps, 4),
+            **aux_bandwidth(tot, args.steps, p.n_q, p.h_q, p.head_dim),
         },
+        # the same work counted without the backward's recompute of S (12d per pair)
+        "value_12d": round(pairs * p.h_q * 12 * p.head_dim / (ms * 1e-3) / 1e12, 2),
+        "ms_per_step_median": round(ms_median, 3),
         "wall_s": round(wall, 3),
     }
     if args.streams > 1:
