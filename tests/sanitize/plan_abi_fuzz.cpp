@@ -247,6 +247,10 @@ void rejections() {
   EXPECT(bdattn_dq_finalize(nullptr, g, 10, nullptr) == BDATTN_EINVAL, "finalize");
   EXPECT(bdattn_cast_f32_bf16(gf, mis, 10, nullptr) == BDATTN_EALIGN, "cast");
   EXPECT(bdattn_plan_export(p, 7, nullptr, 0) == BDATTN_EINVAL, "export which");
+  EXPECT(bdattn_plan_keep_tables(nullptr, g, ws, nullptr) == BDATTN_EINVAL, "keep plan NULL");
+  EXPECT(bdattn_plan_keep_tables(p, mis, ws, nullptr) == BDATTN_EALIGN, "keep misaligned");
+  EXPECT(bdattn_plan_keep_tables(p, g, ws - 1, nullptr) == BDATTN_EWORKSPACE, "keep small");
+  EXPECT(bdattn_plan_keep_tables(p, nullptr, 0, nullptr) == BDATTN_OK, "keep release");
   int32_t a, b, c;
   EXPECT(bdattn_plan_heads(p, &a, &b, &c) == BDATTN_OK && a == 4 && b == 2 && c == 128, "heads");
   EXPECT(bdattn_plan_heads(p, nullptr, &b, &c) == BDATTN_EINVAL, "heads NULL");
