@@ -117,3 +117,48 @@ def test_resident_shards_replayed_from_a_hip_graph():
         for k in OUT:
             assert torch.equal(got[k], want[k]), f"replay {r}: {k}"
         torch.randn(1 << 20, device="cuda").sum().item()   # eager work between replays
+
+
+@pytest.mark.parametrize("lens,causal,split", [([1, 5, 130, 64, 257, 300, 40], True, 0), ([600, 7, 129], False, 3)])
+def test_varlen_plan_over_shard_buffers(lens, causal, split):
+    """A varlen plan whose packed K/V sit in buffers of 128 positions (the last holding
+    the rest; documents span buffer boundaries): bit for bit the one-buffer calls."""
+    from masked_long_context_amd import bdattn as B
+    import numpy as np
+    hq, hkv, d = 4, 2, 128
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cfg = wl.VarlenConfig("t", tuple(lens), hq, hkv, d, causal, 1.0, "")
+    g = {k: v.cuda() for k, v in wl.varlen_inputs(cfg, seed=9).items()}
+    T = int(cu[-1])
+    lens_b = B.shard_split(T, (T + 127) // 128, 128)
+    starts = np.concatenate([[0], np.cumsum(lens_b)])
+    ks = [g["k"][a:b].clone() for a, b in zip(starts[:-1], starts[1:])]
+    vs = [g["v"][a:b].clone() for a, b in zip(starts[:-1], starts[1:])]
+    outs = []
+    for sharded in (False, True):
+        plan = B.Plan.varlen(cu, causal, hq, hkv, d)
+        if split:
+            plan.set_dkdv_split(split)
+        ws = B.workspace(plan.workspace_bytes)
+        o = torch.full((T, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((hq, T), float("nan"), dtype=torch.float32, device="cuda")
+        delta = torch.empty((hq, T), dtype=torch.float32, device="cuda")
+        dq = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
+        if sharded:
+            dks = [torch.full_like(k, float("nan")) for k in ks]
+            dvs = [torch.full_like(v, float("nan")) for v in vs]
+            B.bdattn_fwd_shards(plan, g["q"], ks, vs, None, None, o, lse, ws)
+            B.bdattn_bwd_prepare(plan, o, g["dout"], delta, dq)
+            B.bdattn_bwd_shards(plan, g["q"], ks, vs, None, None, g["dout"], lse, delta, dq, dks, dvs, None, None, ws)
+            dk, dv = torch.cat(dks), torch.cat(dvs)
+        else:
+            dk = torch.full_like(g["k"], float("nan"))
+            dv = torch.full_like(g["v"], float("nan"))
+            B.bdattn_varlen_fwd(plan, g["q"], g["k"], g["v"], o, lse, ws)
+            B.bdattn_bwd_prepare(plan, o, g["dout"], delta, dq)
+            B.bdattn_varlen_bwd(plan, g["q"], g["k"], g["v"], g["dout"], lse, delta, dq, dk, dv, ws)
+        torch.cuda.synchronize()
+        outs.append((o, lse, dq, dk, dv))
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), *outs):
+        assert not torch.isnan(b.float()).any(), f"{name}: unwritten values"
+        assert torch.equal(a, b), name
