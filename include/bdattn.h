@@ -165,7 +165,8 @@ int64_t bdattn_plan_workspace_bytes(const bdattn_plan *plan);
  * as one rank's shard in every training step.  Calls with another workspace
  * upload as before.  A plan keeps at most one workspace (a new call replaces the
  * previous one), and a workspace holds one plan's tables: an upload of another
- * plan's tables into it (any call, or this one) ends the first plan's claim.
+ * plan's tables over any of those bytes (any call, or this one) ends the first
+ * plan's claim.
  * workspace NULL: ends this plan's claim.  The library cannot see other writes:
  * while the tables are kept the caller must not write the workspace (other than
  * through this plan's calls) nor free it; end the claim first (or destroy the

@@ -131,8 +131,8 @@ void fill_shards(const bdattn_kv_shards &kv, bdattn::KvShardTable &t, bdattn::Gr
   }
 }
 
-// Workspaces that hold a kept plan's tables, and the plan; an upload of another
-// plan's tables into one of them ends that plan's claim.
+// Workspaces that hold a kept plan's tables, and the plan: an upload by any plan
+// that overlaps the bytes of another plan's kept tables ends that plan's claim.
 std::mutex g_kept_mu;
 std::unordered_map<const void *, bdattn_plan *> g_kept;
 
@@ -143,11 +143,15 @@ int upload(bdattn_plan *pl, void *dst, hipStream_t stream, bool force = false) {
   {
     std::lock_guard<std::mutex> kl(g_kept_mu);
     auto it = g_kept.find(dst);
-    if (it != g_kept.end()) {
-      if (it->second == pl && !force) return BDATTN_OK;
-      if (it->second != pl) {   // another plan's tables are about to be overwritten
-        it->second->tables_at = nullptr;
-        g_kept.erase(it);
+    if (it != g_kept.end() && it->second == pl && !force) return BDATTN_OK;
+    const uintptr_t lo = (uintptr_t)dst, hi = lo + p.image.size();
+    for (auto k = g_kept.begin(); k != g_kept.end();) {
+      const uintptr_t klo = (uintptr_t)k->first, khi = klo + k->second->p.image.size();
+      if (k->second != pl && klo < hi && lo < khi) {   // those tables are about to be overwritten
+        k->second->tables_at = nullptr;
+        k = g_kept.erase(k);
+      } else {
+        ++k;
       }
     }
   }

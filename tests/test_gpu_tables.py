@@ -49,7 +49,7 @@ def test_another_plans_upload_ends_the_claim():
     g = {k: v.cuda() for k, v in wl.bdlm_inputs(cfg, seed=12).items()}
     pa = B.Plan.from_problem(p.with_kv(0, 512, True))
     pb = B.Plan.from_problem(p.with_kv(512, 512, False))
-    ws = B.workspace(max(pa.workspace_bytes, pb.workspace_bytes))
+    ws = B.workspace(max(pa.workspace_bytes, pb.workspace_bytes) + 256)
     pa.keep_tables(ws)
 
     def fwd_a():
@@ -65,6 +65,14 @@ def test_another_plans_upload_ends_the_claim():
     B.bdattn_fwd(pb, g["q"], g["k_clean"][512:], g["v_clean"][512:], None, None, ob, lb, ws)
     o2, l2 = fwd_a()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # B's tables written 256 bytes into A's kept bytes (another start address) end
+    # A's claim as well
+    pa.keep_tables(ws)
+    inner = ws[256:]
+    assert inner.data_ptr() % 256 == 0 and inner.numel() >= pb.workspace_bytes
+    B.bdattn_fwd(pb, g["q"], g["k_clean"][512:], g["v_clean"][512:], None, None, ob, lb, inner)
+    o4, l4 = fwd_a()
+    assert torch.equal(o1, o4) and torch.equal(l1, l4)
     # and a fresh workspace (no claim) gives the same bits
     ws2 = B.workspace(pa.workspace_bytes)
     o3 = torch.empty_like(o1)
