@@ -63,17 +63,18 @@ class BdlmRankStep:
         self.active = [i for i, pl in enumerate(self.plans) if pl.useful_pairs > 0]
         p = problem
         self.n_q, self.h_q, self.h_kv, self.d = p.n_q, p.h_q, p.h_kv, p.head_dim
-        ws_bytes = max(pl.workspace_bytes for pl in self.plans)
-        self.ws = B.workspace(ws_bytes, device)
         # streams > 1: the per-shard forward and dK/dV calls, which are independent,
         # alternate over the caller's stream and streams - 1 side streams (default
         # priority), each with its own workspace; the dQ calls, which add into one
         # accumulator, stay on the caller's stream in shard order
         self.side = [torch.cuda.Stream(device=device) for _ in range(max(1, int(streams)) - 1)]
-        self.ws_side = [B.workspace(ws_bytes, device) for _ in self.side]
         # keep_tables: every plan keeps its tables in a workspace of its own, uploaded
-        # once here, so no call of a step waits for a table upload
+        # once here, so no call of a step waits for a table upload; otherwise one
+        # workspace per stream, into which every call uploads its plan's tables
         self.ws_plan = keep_workspaces(self.plans, device) if keep_tables else None
+        ws_bytes = max(pl.workspace_bytes for pl in self.plans)
+        self.ws = None if keep_tables else B.workspace(ws_bytes, device)
+        self.ws_side = [] if keep_tables else [B.workspace(ws_bytes, device) for _ in self.side]
         # one active shard: its forward writes O and LSE itself (no partials)
         self.direct = len(self.active) == 1
         n_parts = 0 if self.direct else max(1, len(self.active))
