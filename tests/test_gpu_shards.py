@@ -119,10 +119,16 @@ def test_resident_shards_replayed_from_a_hip_graph():
         torch.randn(1 << 20, device="cuda").sum().item()   # eager work between replays
 
 
-@pytest.mark.parametrize("lens,causal,split", [([1, 5, 130, 64, 257, 300, 40], True, 0), ([600, 7, 129], False, 3)])
-def test_varlen_plan_over_shard_buffers(lens, causal, split):
-    """A varlen plan whose packed K/V sit in buffers of 128 positions (the last holding
-    the rest; documents span buffer boundaries): bit for bit the one-buffer calls."""
+@pytest.mark.parametrize("lens,causal,split,tasks", [
+    ([1, 5, 130, 64, 257, 300, 40], True, 0, False),
+    ([600, 7, 129], False, 3, False),
+    ([2000, 37], True, 0, False),              # 2037 keys: the full table of 16 buffers
+    ([130, 64, 257, 900], True, 0, True),      # core-attention tasks with prefix contexts
+])
+def test_varlen_plan_over_shard_buffers(lens, causal, split, tasks):
+    """A varlen (or task) plan whose packed K/V sit in buffers of 128 positions or more
+    (the last holding the rest; documents span buffer boundaries): bit for bit the
+    one-buffer calls."""
     from masked_long_context_amd import bdattn as B
     import numpy as np
     hq, hkv, d = 4, 2, 128
@@ -130,13 +136,22 @@ def test_varlen_plan_over_shard_buffers(lens, causal, split):
     cfg = wl.VarlenConfig("t", tuple(lens), hq, hkv, d, causal, 1.0, "")
     g = {k: v.cuda() for k, v in wl.varlen_inputs(cfg, seed=9).items()}
     T = int(cu[-1])
-    lens_b = B.shard_split(T, (T + 127) // 128, 128)
+    if tasks:
+        # the documents as bounded tasks, each carrying its prefix context (gathered keys)
+        q_cu, k_cu, src = B.cad_split(cu, 20000)
+        rows = wl.task_context_rows(k_cu, src)
+        g["k"], g["v"] = g["k"][torch.from_numpy(rows).long().cuda()], g["v"][torch.from_numpy(rows).long().cuda()]
+        assert int(q_cu[-1]) == T and len(q_cu) > len(cu)
+    n_keys = int(g["k"].shape[0])
+    # buffers of 128 positions, or the smallest multiple of 128 that needs at most 16
+    blen = max(128, -(-n_keys // (B.MAX_SHARDS * 128)) * 128)
+    lens_b = B.shard_split(n_keys, -(-n_keys // blen), blen)
     starts = np.concatenate([[0], np.cumsum(lens_b)])
     ks = [g["k"][a:b].clone() for a, b in zip(starts[:-1], starts[1:])]
     vs = [g["v"][a:b].clone() for a, b in zip(starts[:-1], starts[1:])]
     outs = []
     for sharded in (False, True):
-        plan = B.Plan.varlen(cu, causal, hq, hkv, d)
+        plan = B.Plan.tasks(q_cu, k_cu, causal, hq, hkv, d) if tasks else B.Plan.varlen(cu, causal, hq, hkv, d)
         if split:
             plan.set_dkdv_split(split)
         ws = B.workspace(plan.workspace_bytes)
@@ -154,6 +169,7 @@ def test_varlen_plan_over_shard_buffers(lens, causal, split):
         else:
             dk = torch.full_like(g["k"], float("nan"))
             dv = torch.full_like(g["v"], float("nan"))
+            assert plan.n_kv(0) == n_keys
             B.bdattn_varlen_fwd(plan, g["q"], g["k"], g["v"], o, lse, ws)
             B.bdattn_bwd_prepare(plan, o, g["dout"], delta, dq)
             B.bdattn_varlen_bwd(plan, g["q"], g["k"], g["v"], g["dout"], lse, delta, dq, dk, dv, ws)
