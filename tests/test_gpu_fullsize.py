@@ -213,6 +213,36 @@ def test_csbp_1m_rank_share_fullsize():
     run_bdlm_fullsize(5, n_rows=4096)
 
 
+def test_csbp_1m_resident_shards_match_one_buffer():
+    """The 1M-context rank share with its 8 clean shards resident in buffers of 131072
+    positions, one launch per kernel: bit for bit the same plan over one buffer (the
+    split-buffer kernels at their largest in-buffer offsets)."""
+    need_gpu()
+    cfg = wl.config(5)
+    p = cfg.problem
+    log(f"{cfg.name}: generating inputs")
+    g = {k: v.cuda() for k, v in wl.bdlm_inputs(cfg, seed=0).items()}
+    step = ResidentShardsStep(p, cfg.shards)
+    k_sh = [g["k_clean"][o_:o_ + n_].clone() for (o_, n_, _) in cfg.shards]
+    v_sh = [g["v_clean"][o_:o_ + n_].clone() for (o_, n_, _) in cfg.shards]
+    assert step.shard_lens == [131072] * 8
+    log(f"{cfg.name}: GPU step (8 resident shard buffers)")
+    step.step(g["q"], k_sh, v_sh, g["k_corr"], g["v_corr"], g["dout"])
+    torch.cuda.synchronize()
+    got = [step.o.cpu(), step.lse.cpu(), step.dq.cpu(), torch.cat(step.dk_shards + [step.dk_corr]).cpu(),
+           torch.cat(step.dv_shards + [step.dv_corr]).cpu()]
+    del step, k_sh, v_sh
+    one = BdlmRankStep(p, [(0, p.clean_len, True)])
+    log(f"{cfg.name}: GPU step (one buffer, the same plan)")
+    one.step(g["q"], g["k_clean"], g["v_clean"], g["k_corr"], g["v_corr"], g["dout"])
+    torch.cuda.synchronize()
+    want = [one.o, one.lse, one.dq, torch.cat([one.dk_clean, one.dk_corr]), torch.cat([one.dv_clean, one.dv_corr])]
+    for name, a_, b_ in zip(("o", "lse", "dq", "dk", "dv"), got, want):
+        assert not torch.isnan(a_.float()).any(), f"{name}: unwritten values"
+        assert torch.equal(a_, b_.cpu()), f"resident shards vs one buffer: {name} differs"
+    log(f"{cfg.name}: resident shards and one buffer agree bit for bit")
+
+
 def test_varlen_262k_fullsize():
     need_gpu()
     cfg = wl.config(4)
